@@ -1,0 +1,280 @@
+/*
+ * dsa_oracle.c -- plain CPU definition of the DeepSeek Sparse Attention
+ * decode hot path (lightning-indexer scores, top-k selection, absorbed-MLA
+ * attention over the selection, and the pooled "k-pool" NoPE variant).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the oracle that the HIP path is
+ * checked against.  Only the test-suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code, header, table or helper with the HIP library: it is built
+ * by gcc from this one file.
+ *
+ * Precision: every floating-point sum is formed in double from the bf16
+ * inputs and rounded to float once, when stored.  With integer-valued
+ * indexer inputs (as in every workload here) the scores are exact.
+ *
+ * Sources (pages on GLM-5.x and DeepSeek Sparse Attention):
+ *  [TS]  TensorSharp2 docs, "GLM-5.x (glm-dsa, glm5next)": table "The block";
+ *        section "The sparse-attention path"; section "GLM-5.3-Flash
+ *        (glm5next)" and its table.
+ *  [PC]  "GLM 5.2 in pure C" (Medium): sections "Attention: Multi head Latent
+ *        Attention With a Tiny KV Cache" and "The Lightning Indexer: Sparse
+ *        Attention When It Helps".
+ *  [WA]  "GLM-5.3-Flash on WASTE" (sqliteai/warp docs/GLM.md): section
+ *        "DeepSeek Sparse Attention, k-pool flavour".
+ *  [ST]  Strata PR "Add GLM-5.3-Flash (glm5-next) support": "What a glm5-next
+ *        block has that nothing else in the engine does"; "Known gaps".
+ *
+ * Readings taken where the pages are silent or disagree (each is listed in
+ * the design notes as well):
+ *  - the score carries no 1/sqrt(128) or 1/sqrt(32) factor: the problem
+ *    statement's score is sum_h w_h * relu(q_h . k); positive constants do
+ *    not change the ranking and a caller may fold them into w;
+ *  - top-k keeps exactly min(k, n) rows: everything ranked at or above the
+ *    k-th under the total order (score descending, index ascending), so
+ *    equal scores go to the lower index;
+ *  - the selection is reported in ascending token order, padded with -1;
+ *  - k-pool: dense (every visible token) while the complete pools number at
+ *    most top_k/kpool; otherwise the best top_k/kpool pools, expanded to
+ *    their tokens, plus the unpooled tail [kpool*n_pools, n_vis) always;
+ *  - the softmax scale multiplies the whole 576-wide (or 512-wide) dot; V is
+ *    the first d_latent columns of the selected rows.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 is the upper half of an IEEE float: widen it exactly. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Indexer score of every visible row ([PC] "The Lightning Indexer": a
+ * rectified dot product per indexer head, then a weighted sum across heads;
+ * [TS] "The block": 32 indexer heads of width 128 score every cached token).
+ *
+ *   s[q][r] = sum_{h < n_idx_heads} w[q][h] * max(0, sum_{d < d_idx} qi[q][h][d] * K[seq(q)][r][d])
+ *
+ * for r < rows(q) = q_nvis[q] / kpool.  Rows are tokens (kpool = 1) or
+ * complete pools of kpool tokens ([WA] "k-pool flavour": one compressed
+ * 128-wide key per pool).  Entries of s at r >= rows(q) are left untouched.
+ */
+int oracle_index_scores(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
+                        int32_t kpool, int32_t n_idx_heads, int32_t d_idx,
+                        const uint16_t *idx_q, const float *idx_w,
+                        const uint16_t *idx_k, int64_t key_seq_stride,
+                        float *scores, int64_t score_ld)
+{
+    for (int32_t q = 0; q < n_q; q++) {
+        const int64_t rows = q_nvis[q] / kpool;
+        const int64_t seq = q_seq ? q_seq[q] : q;
+        const uint16_t *qi = idx_q + (int64_t)q * n_idx_heads * d_idx;
+        const float *w = idx_w + (int64_t)q * n_idx_heads;
+        const uint16_t *K = idx_k + seq * key_seq_stride * d_idx;
+        #pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows; r++) {
+            const uint16_t *k = K + r * d_idx;
+            double acc = 0.0;
+            for (int32_t h = 0; h < n_idx_heads; h++) {
+                double dot = 0.0;
+                for (int32_t d = 0; d < d_idx; d++)
+                    dot += bf16_value(qi[h * d_idx + d]) * bf16_value(k[d]);
+                if (dot > 0.0)
+                    acc += (double)w[h] * dot;
+            }
+            scores[(int64_t)q * score_ld + r] = (float)acc;
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    float s;
+    int64_t r;
+} scored_row;
+
+/* Total order of the selection: higher score first, equal scores by lower
+ * index ([WA] "k-pool flavour": ties are ordered by index upstream).  The
+ * float comparison treats -0 and +0 as equal. */
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const scored_row *a = (const scored_row *)pa, *b = (const scored_row *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->r > b->r) - (a->r < b->r);
+}
+
+static int by_index(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Top-k selection ([PC] "The Lightning Indexer": keep the best index_topk
+ * positions, and with fewer visible keys than that keep them all -- the dense
+ * case of [TS] "The sparse-attention path"; [WA] "k-pool flavour": keep the
+ * best index_topk/index_kpool pools, attend their tokens plus the tail that
+ * has not filled a pool; [ST] "Known gaps": the tail is appended).
+ *
+ * Output per query: sel[q][0..count) in ascending token order, the rest of
+ * the sel_ld slots set to -1; sel_count[q] = count.
+ * Returns 0, or -1 if sel_ld cannot hold a selection.
+ */
+int oracle_topk(int32_t n_q, const int32_t *q_nvis, int32_t kpool, int32_t top_k,
+                const float *scores, int64_t score_ld,
+                int32_t *sel, int32_t sel_ld, int32_t *sel_count)
+{
+    const int64_t keep = top_k / kpool;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int32_t q = 0; q < n_q; q++) {
+        const int64_t n_vis = q_nvis[q];
+        const int64_t rows = n_vis / kpool;
+        int32_t *dst = sel + (int64_t)q * sel_ld;
+        int64_t count = 0;
+        if (rows <= keep) {
+            /* nothing to remove: every visible token */
+            if (n_vis > sel_ld) { bad = 1; continue; }
+            for (int64_t t = 0; t < n_vis; t++)
+                dst[count++] = (int32_t)t;
+        } else {
+            scored_row *all = (scored_row *)malloc((size_t)rows * sizeof *all);
+            int64_t *pick = (int64_t *)malloc((size_t)keep * sizeof *pick);
+            for (int64_t r = 0; r < rows; r++) {
+                all[r].s = scores[(int64_t)q * score_ld + r];
+                all[r].r = r;
+            }
+            qsort(all, (size_t)rows, sizeof *all, by_score_then_index);
+            for (int64_t i = 0; i < keep; i++)
+                pick[i] = all[i].r;
+            qsort(pick, (size_t)keep, sizeof *pick, by_index);
+            const int64_t tail = n_vis - rows * kpool;
+            if (keep * kpool + tail > sel_ld) {
+                bad = 1;
+            } else {
+                for (int64_t i = 0; i < keep; i++)
+                    for (int64_t j = 0; j < kpool; j++)
+                        dst[count++] = (int32_t)(pick[i] * kpool + j);
+                for (int64_t t = rows * kpool; t < n_vis; t++)
+                    dst[count++] = (int32_t)t;
+            }
+            free(all);
+            free(pick);
+        }
+        sel_count[q] = (int32_t)count;
+        for (int64_t i = count; i < sel_ld; i++)
+            dst[i] = -1;
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Absorbed-MLA attention over the selected rows ([PC] "Attention: Multi head
+ * Latent Attention With a Tiny KV Cache": the absorbed query is dotted with
+ * the latent and the rotary part of each cached row, scaled, softmaxed, and
+ * the latents are pooled with those weights; [TS] "The block": one 576-wide
+ * row per token, 64 query heads and one key head, softmax scale 1/16;
+ * [TS] "GLM-5.3-Flash" and [ST]: NoPE rows are the 512-wide latent alone).
+ *
+ * For query q, head h, and each selected token t:
+ *   z_t = scale * sum_{d < D} qt[q][h][d] * C[seq(q)][t][d],  D = d_latent + d_rope
+ *   out[q][h][j] = sum_t exp(z_t - m) * C[t][j] / sum_t exp(z_t - m),  j < d_latent
+ *   lse[q][h]   = m + log(sum_t exp(z_t - m)),  m = max_t z_t
+ */
+int oracle_mla_attend(int32_t n_q, const int32_t *q_seq, int32_t n_heads,
+                      int32_t d_latent, int32_t d_rope, float scale,
+                      const uint16_t *q, const uint16_t *cache, int64_t cache_seq_stride,
+                      const int32_t *sel, int32_t sel_ld, const int32_t *sel_count,
+                      float *out, float *lse)
+{
+    const int32_t D = d_latent + d_rope;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int32_t qq = 0; qq < n_q; qq++) {
+        for (int32_t h = 0; h < n_heads; h++) {
+            const int64_t seq = q_seq ? q_seq[qq] : qq;
+            const int32_t n = sel_count[qq];
+            const int32_t *rows = sel + (int64_t)qq * sel_ld;
+            const uint16_t *qh = q + ((int64_t)qq * n_heads + h) * D;
+            const uint16_t *C = cache + seq * cache_seq_stride * D;
+            double *z = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof *z);
+            double *o = (double *)calloc((size_t)d_latent, sizeof *o);
+            double m = -INFINITY;
+            for (int32_t i = 0; i < n; i++) {
+                const uint16_t *c = C + (int64_t)rows[i] * D;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D; d++)
+                    dot += bf16_value(qh[d]) * bf16_value(c[d]);
+                z[i] = (double)scale * dot;
+                if (z[i] > m) m = z[i];
+            }
+            double l = 0.0;
+            for (int32_t i = 0; i < n; i++) {
+                const double p = exp(z[i] - m);
+                const uint16_t *c = C + (int64_t)rows[i] * D;
+                l += p;
+                for (int32_t j = 0; j < d_latent; j++)
+                    o[j] += p * bf16_value(c[j]);
+            }
+            float *dst = out + ((int64_t)qq * n_heads + h) * d_latent;
+            for (int32_t j = 0; j < d_latent; j++)
+                dst[j] = (float)(o[j] / l);
+            if (lse)
+                lse[(int64_t)qq * n_heads + h] = (float)(m + log(l));
+            free(z);
+            free(o);
+        }
+    }
+    return 0;
+}
+
+/*
+ * One decode (or prefill-chunk) step: scores, then top-k, then attention,
+ * for every query of the batch ([TS] "The sparse-attention path": below
+ * top_k cached tokens the scoring is skipped and attention is dense, which
+ * the top-k definition above already yields).  Scores live in a scratch
+ * buffer owned by this call.  sel/sel_count are outputs (caller-sized).
+ */
+int oracle_decode_step(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
+                       int32_t kpool, int32_t top_k, int32_t n_heads,
+                       int32_t d_latent, int32_t d_rope, float scale,
+                       int32_t n_idx_heads, int32_t d_idx,
+                       const uint16_t *idx_q, const float *idx_w,
+                       const uint16_t *idx_k, int64_t key_seq_stride,
+                       const uint16_t *q, const uint16_t *cache, int64_t cache_seq_stride,
+                       int32_t *sel, int32_t sel_ld, int32_t *sel_count,
+                       float *out, float *lse)
+{
+    int64_t max_rows = 1;
+    for (int32_t i = 0; i < n_q; i++)
+        if (q_nvis[i] / kpool > max_rows) max_rows = q_nvis[i] / kpool;
+    float *scores = (float *)malloc((size_t)n_q * (size_t)max_rows * sizeof *scores);
+    if (!scores) return -2;
+    int rc = oracle_index_scores(n_q, q_seq, q_nvis, kpool, n_idx_heads, d_idx,
+                                 idx_q, idx_w, idx_k, key_seq_stride, scores, max_rows);
+    if (rc == 0)
+        rc = oracle_topk(n_q, q_nvis, kpool, top_k, scores, max_rows, sel, sel_ld, sel_count);
+    if (rc == 0)
+        rc = oracle_mla_attend(n_q, q_seq, n_heads, d_latent, d_rope, scale, q, cache,
+                               cache_seq_stride, sel, sel_ld, sel_count, out, lse);
+    free(scores);
+    return rc;
+}

@@ -1,0 +1,140 @@
+"""ctypes front of the C oracle (``dsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path may
+not.  It imports nothing from the HIP package.  All arrays are numpy, bf16
+tensors are passed as their raw uint16 bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "dsa_oracle.c")
+LIB = os.path.join(HERE, "libdsa_oracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (OpenMP over queries / rows)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                               "-fPIC", "-shared", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def load(path: str):
+    """Load an oracle shared library and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.oracle_index_scores.argtypes = [i32, P, P, i32, i32, i32, P, P, P, i64, P, i64]
+    L.oracle_topk.argtypes = [i32, P, i32, i32, P, i64, P, i32, P]
+    L.oracle_mla_attend.argtypes = [i32, P, i32, i32, i32, f32, P, P, i64, P, i32, P, P, P]
+    L.oracle_decode_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f32, i32, i32,
+                                     P, P, P, i64, P, P, i64, P, i32, P, P, P]
+    L.oracle_max_threads.argtypes = []
+    for f in (L.oracle_index_scores, L.oracle_topk, L.oracle_mla_attend,
+              L.oracle_decode_step, L.oracle_max_threads):
+        f.restype = ctypes.c_int
+    return L
+
+
+_default = None
+
+
+def lib():
+    global _default
+    if _default is None:
+        _default = load(build())
+    return _default
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads(L=None) -> int:
+    return int((L or lib()).oracle_max_threads())
+
+
+def index_scores(q_seq, q_nvis, kpool, idx_q, idx_w, idx_k, score_ld=None, fill=np.nan, L=None):
+    """Scores [n_q, score_ld] float32; entries past rows(q) hold ``fill``.
+
+    idx_q: uint16 [n_q, HI, DI]; idx_w: float32 [n_q, HI];
+    idx_k: uint16 [n_seq, key_rows, DI]."""
+    q_seq, q_nvis = _c(q_seq, np.int32), _c(q_nvis, np.int32)
+    idx_q, idx_w, idx_k = _c(idx_q, np.uint16), _c(idx_w, np.float32), _c(idx_k, np.uint16)
+    n_q, HI, DI = idx_q.shape
+    if score_ld is None:
+        score_ld = max(1, int(q_nvis.max()) // kpool)
+    out = np.full((n_q, score_ld), fill, dtype=np.float32)
+    rc = (L or lib()).oracle_index_scores(n_q, _p(q_seq), _p(q_nvis), kpool, HI, DI, _p(idx_q),
+                                   _p(idx_w), _p(idx_k), idx_k.shape[1], _p(out), score_ld)
+    assert rc == 0
+    return out
+
+
+def topk(q_nvis, kpool, top_k, scores, sel_ld=None, L=None):
+    """Returns (sel int32 [n_q, sel_ld] ascending, padded -1; count int32 [n_q])."""
+    q_nvis = _c(q_nvis, np.int32)
+    scores = _c(scores, np.float32)
+    n_q = q_nvis.shape[0]
+    if sel_ld is None:
+        sel_ld = top_k + kpool - 1
+    sel = np.empty((n_q, sel_ld), dtype=np.int32)
+    cnt = np.empty(n_q, dtype=np.int32)
+    rc = (L or lib()).oracle_topk(n_q, _p(q_nvis), kpool, top_k, _p(scores), scores.shape[1],
+                           _p(sel), sel_ld, _p(cnt))
+    if rc != 0:
+        raise ValueError("sel_ld too small for the selection")
+    return sel, cnt
+
+
+def mla_attend(q_seq, d_latent, d_rope, scale, q, cache, sel, sel_count, want_lse=True, L=None):
+    """Returns (out float32 [n_q, H, d_latent], lse float32 [n_q, H] or None).
+
+    q: uint16 [n_q, H, D]; cache: uint16 [n_seq, T, D]."""
+    q_seq = _c(q_seq, np.int32)
+    q, cache = _c(q, np.uint16), _c(cache, np.uint16)
+    sel, sel_count = _c(sel, np.int32), _c(sel_count, np.int32)
+    n_q, H, D = q.shape
+    assert D == d_latent + d_rope and cache.shape[2] == D
+    out = np.empty((n_q, H, d_latent), dtype=np.float32)
+    lse = np.empty((n_q, H), dtype=np.float32) if want_lse else None
+    rc = (L or lib()).oracle_mla_attend(n_q, _p(q_seq), H, d_latent, d_rope, float(scale), _p(q),
+                                 _p(cache), cache.shape[1], _p(sel), sel.shape[1],
+                                 _p(sel_count), _p(out), _p(lse))
+    assert rc == 0
+    return out, lse
+
+
+def decode_step(geom, q_seq, q_nvis, idx_q, idx_w, idx_k, q, cache, sel_ld=None, L=None):
+    """Full step for every query.  Returns (sel, sel_count, out, lse)."""
+    q_seq, q_nvis = _c(q_seq, np.int32), _c(q_nvis, np.int32)
+    idx_q, idx_w, idx_k = _c(idx_q, np.uint16), _c(idx_w, np.float32), _c(idx_k, np.uint16)
+    q, cache = _c(q, np.uint16), _c(cache, np.uint16)
+    kpool, top_k = geom["kpool"], geom["top_k"]
+    n_q, H, D = q.shape
+    if sel_ld is None:
+        sel_ld = top_k + kpool - 1
+    sel = np.empty((n_q, sel_ld), dtype=np.int32)
+    cnt = np.empty(n_q, dtype=np.int32)
+    out = np.empty((n_q, H, geom["d_latent"]), dtype=np.float32)
+    lse = np.empty((n_q, H), dtype=np.float32)
+    rc = (L or lib()).oracle_decode_step(n_q, _p(q_seq), _p(q_nvis), kpool, top_k, H,
+                                  geom["d_latent"], geom["d_rope"], float(geom["softmax_scale"]),
+                                  idx_q.shape[1], idx_q.shape[2], _p(idx_q), _p(idx_w),
+                                  _p(idx_k), idx_k.shape[1], _p(q), _p(cache), cache.shape[1],
+                                  _p(sel), sel_ld, _p(cnt), _p(out), _p(lse))
+    assert rc == 0
+    return sel, cnt, out, lse

@@ -1,0 +1,334 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function takes an oracle library handle (``oracle.load``) and
+raises AssertionError when the oracle disagrees with what the pages and the
+mathematics fix: integer closed forms, an independent library routine
+(numpy's integer matmul, ``lexsort``, float64 softmax), invariants and
+hand-derived small cases.  ``test_oracle_pins.py`` runs them on the real
+oracle; ``test_oracle_mutants.py`` runs them on deliberately broken copies
+of the oracle source and requires that every copy fails at least one pin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import oracle as O
+from deepseek_sparse_attention_amd.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+
+HI, DI, H = 32, 128, 64
+
+
+def bf(x):
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def fl(b):
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+# ---------------------------------------------------------------- brute force
+def brute_scores(qi_int, w, K_int, rows):
+    """s = relu(K qi^T) w in exact integer arithmetic (numpy int64 matmul)."""
+    dots = K_int[:rows].astype(np.int64) @ qi_int.astype(np.int64).T      # [rows, HI]
+    return np.maximum(dots, 0) @ w.astype(np.int64)
+
+
+def brute_select(s, n_vis, kpool, top_k, ties_high=False, strict=False, tail=True,
+                 dense_fallback=True, order="index"):
+    """Reference selection by full lexsort.  Keyword switches give the rival
+    readings that the pages' text leaves room for; the defaults are the
+    reading the oracle implements."""
+    rows, keep = n_vis // kpool, top_k // kpool
+    if dense_fallback and rows <= keep:
+        return list(range(n_vis))
+    idx = np.arange(rows)
+    sc = np.asarray(s[:rows], dtype=np.float64)
+    if ties_high:
+        order_ = np.lexsort((-idx, -sc))
+    else:
+        order_ = np.lexsort((idx, -sc))
+    picked = order_[:min(keep, rows)]
+    if strict:   # keep only rows strictly above the keep-th score
+        thr = sc[order_[min(keep, rows) - 1]]
+        picked = idx[sc > thr]
+    if order == "index":
+        picked = np.sort(picked)
+    out = [int(p) * kpool + j for p in picked for j in range(kpool)]
+    if tail:
+        out += list(range(rows * kpool, n_vis))
+    return out
+
+
+def brute_attend(qh, C, sel, scale, d_latent):
+    """Softmax attention of one head over selected rows, float64."""
+    rows = C[np.asarray(sel)]
+    z = scale * (rows @ qh)
+    m = z.max()
+    p = np.exp(z - m)
+    o = (p @ rows[:, :d_latent]) / p.sum()
+    return o, m + math.log(p.sum())
+
+
+# ---------------------------------------------------------------- scores
+def pin_scores_integer_closed_form(L):
+    """Integer inputs: the score is exact, so it must equal the int64 brute
+    force bit for bit, for tokens and for pools, with negative and zero head
+    weights (which separate ReLU-then-weight from weight-then-ReLU)."""
+    rng = np.random.default_rng(101)
+    for kpool, key_rows, nvis in ((1, 300, [300, 257, 1]), (4, 75, [300, 259, 7])):
+        qi = rng.integers(-8, 9, size=(3, HI, DI))
+        K = rng.integers(-8, 9, size=(2, key_rows, DI))
+        w = rng.integers(-2, 5, size=(3, HI))
+        q_seq = np.array([0, 1, 1])
+        s = O.index_scores(q_seq, nvis, kpool, bf(qi), w.astype(np.float32), bf(K), L=L)
+        for j in range(3):
+            rows = nvis[j] // kpool
+            ref = brute_scores(qi[j], w[j], K[q_seq[j]], rows)
+            assert np.array_equal(s[j, :rows], ref.astype(np.float32)), (kpool, j)
+            assert np.isnan(s[j, rows:]).all(), "wrote past the visible rows"
+
+
+def pin_scores_hand_case(L):
+    """Two active heads, hand-derived: head 0 has q=2 at d=0 and weight 3,
+    head 1 has q=-1 at d=1 and weight 5; key r has k[0]=r-2, k[1]=1-r.
+    s(r) = 3*max(0, 2(r-2)) + 5*max(0, r-1) = 0, 0, 5, 16, 27 for r=0..4."""
+    qi = np.zeros((1, HI, DI))
+    qi[0, 0, 0], qi[0, 1, 1] = 2, -1
+    w = np.zeros((1, HI), dtype=np.float32)
+    w[0, 0], w[0, 1] = 3, 5
+    K = np.zeros((1, 5, DI))
+    K[0, :, 0] = np.arange(5) - 2
+    K[0, :, 1] = 1 - np.arange(5)
+    s = O.index_scores([0], [5], 1, bf(qi), w, bf(K), L=L)
+    assert s[0].tolist() == [0.0, 0.0, 5.0, 16.0, 27.0], s
+
+
+def pin_scores_real_valued(L):
+    """Real-valued inputs: equal to a float64 numpy evaluation rounded once."""
+    rng = np.random.default_rng(7)
+    qi = fl(bf(rng.standard_normal((2, HI, DI))))
+    K = fl(bf(rng.standard_normal((1, 64, DI))))
+    w = rng.standard_normal((2, HI)).astype(np.float32)
+    s = O.index_scores([0, 0], [64, 33], 1, bf(qi), w, bf(K), L=L)
+    for j, rows in enumerate((64, 33)):
+        ref = np.maximum(K[0, :rows] @ qi[j].T, 0) @ w[j].astype(np.float64)
+        assert np.allclose(s[j, :rows], ref, rtol=1e-6, atol=1e-5)
+
+
+# ---------------------------------------------------------------- top-k
+def _check_topk_against_brute(L, s_rows, n_vis, kpool, top_k):
+    n_q = len(n_vis)
+    sel, cnt = O.topk(n_vis, kpool, top_k, s_rows, L=L)
+    for j in range(n_q):
+        ref = brute_select(s_rows[j], n_vis[j], kpool, top_k)
+        got = sel[j, :cnt[j]].tolist()
+        assert got == ref, (kpool, top_k, n_vis[j], got[:16], ref[:16])
+        assert (sel[j, cnt[j]:] == -1).all()
+
+
+def pin_topk_straddle_sweep(L):
+    """Every visible count around the budget, token and pool level, with
+    score vectors full of equal values (ties resolved by lower index)."""
+    rng = np.random.default_rng(5)
+    for kpool, tops in ((1, (1, 2, 3, 8, 16, 64)), (4, (4, 8, 16, 64))):
+        for top_k in tops:
+            keep = top_k // kpool
+            lo = max(1, (keep - 3) * kpool)
+            hi = (keep + 4) * kpool + kpool
+            n_vis = list(range(lo, hi + 1))
+            rows_max = max(n_vis) // kpool
+            s = rng.integers(0, 4, size=(len(n_vis), max(rows_max, 1))).astype(np.float32)
+            _check_topk_against_brute(L, s, n_vis, kpool, top_k)
+
+
+def pin_topk_large_random(L):
+    """Larger random cases, real and integer valued, against lexsort."""
+    rng = np.random.default_rng(9)
+    s_real = rng.standard_normal((3, 5000)).astype(np.float32)
+    _check_topk_against_brute(L, s_real, [5000, 4097, 2049], 1, 2048)
+    s_int = rng.integers(0, 50, size=(3, 5000)).astype(np.float32)
+    _check_topk_against_brute(L, s_int, [5000, 4999, 3000], 1, 2048)
+    s_pool = rng.integers(0, 20, size=(2, 1300)).astype(np.float32)
+    _check_topk_against_brute(L, s_pool, [5203, 2052], 4, 2048)
+
+
+def pin_topk_signed_zero(L):
+    """-0.0 and +0.0 are the same score: the lower index wins the tie."""
+    s = np.array([[-0.0, 0.0, -0.0, 1.0, 0.0]], dtype=np.float32)
+    sel, cnt = O.topk([5], 1, 3, s, L=L)
+    assert sel[0, :cnt[0]].tolist() == [0, 1, 3]
+
+
+def pin_topk_written_rows(L):
+    """Hand-written expected rows; each fixture also separates the oracle's
+    reading from a rival one that the pages leave room for."""
+    s = np.array([[5, 7, 7, 1, 7, 0, 3, 7]], dtype=np.float32)
+    sel, cnt = O.topk([8], 1, 3, s, L=L)
+    assert sel[0, :cnt[0]].tolist() == [1, 2, 4]
+    assert brute_select(s[0], 8, 1, 3, ties_high=True) == [2, 4, 7]
+    assert brute_select(s[0], 8, 1, 3, strict=True) == []        # all four 7s tie at the k-th
+    assert brute_select(s[0], 8, 1, 3, order="score") == [1, 2, 4]
+    s2 = np.array([[1, 9, 4, 9, 2, 8]], dtype=np.float32)
+    sel, cnt = O.topk([6], 1, 3, s2, L=L)
+    assert sel[0, :cnt[0]].tolist() == [1, 3, 5]
+    assert brute_select(s2[0], 6, 1, 3, strict=True) == [1, 3]
+    # pools of 4, keep one pool: equal pool scores go to pool 0; tail appended
+    sp = np.array([[3, 3]], dtype=np.float32)
+    sel, cnt = O.topk([11], 4, 4, sp, L=L)
+    assert sel[0, :cnt[0]].tolist() == [0, 1, 2, 3, 8, 9, 10]
+    assert brute_select(sp[0], 11, 4, 4, ties_high=True) == [4, 5, 6, 7, 8, 9, 10]
+    assert brute_select(sp[0], 11, 4, 4, tail=False) == [0, 1, 2, 3]
+    # exactly at the budget: dense, every visible token including the tail
+    sel, cnt = O.topk([7], 4, 4, np.array([[1.0]], dtype=np.float32), L=L)
+    assert sel[0, :cnt[0]].tolist() == list(range(7))
+    sel, cnt = O.topk([8], 4, 4, np.array([[1.0, 2.0]], dtype=np.float32), L=L)
+    assert sel[0, :cnt[0]].tolist() == [4, 5, 6, 7]
+    # dense below k at token level, whatever the scores
+    sel, cnt = O.topk([3], 1, 4, np.array([[9.0, -1.0, 2.0]], dtype=np.float32), L=L)
+    assert sel[0, :cnt[0]].tolist() == [0, 1, 2]
+    assert brute_select([9.0, -1.0, 2.0], 3, 1, 4, dense_fallback=False) == [0, 1, 2]
+
+
+def pin_topk_invariants(L):
+    """|S| = min(k, n); every selected score >= every unselected one; among
+    scores equal to the smallest selected one, the selected have the lowest
+    indices."""
+    rng = np.random.default_rng(11)
+    n, k = 6000, 2048
+    s = rng.integers(0, 300, size=(1, n)).astype(np.float32)
+    sel, cnt = O.topk([n], 1, k, s, L=L)
+    S = sel[0, :cnt[0]]
+    assert cnt[0] == k and len(set(S.tolist())) == k
+    mask = np.zeros(n, bool)
+    mask[S] = True
+    thr = s[0, S].min()
+    assert s[0, mask].min() >= s[0, ~mask].max()
+    eq = np.nonzero(s[0] == thr)[0]
+    taken = eq[mask[eq]]
+    assert (taken == eq[:len(taken)]).all()
+
+
+# ---------------------------------------------------------------- attention
+def pin_attend_dense_matches_softmax(L):
+    """k >= n_vis: attention over the selection is dense masked softmax
+    attention, computed independently in float64 with numpy."""
+    rng = np.random.default_rng(3)
+    T, D, dl = 100, 576, 512
+    C = bf(rng.standard_normal((2, T, D)))
+    q = bf(rng.standard_normal((2, H, D)))
+    sel = np.full((2, 2048), -1, np.int32)
+    sel[0, :100] = np.arange(100)
+    picks = np.sort(rng.choice(T, 37, replace=False))
+    sel[1, :37] = picks
+    cnt = np.array([100, 37], np.int32)
+    out, lse = O.mla_attend([0, 1], dl, 64, 1 / 16, q, C, sel, cnt, L=L)
+    Cf, qf = fl(C), fl(q)
+    for j, (s_, c_) in enumerate(((0, sel[0, :100]), (1, picks))):
+        for h in range(H):
+            o, l_ = brute_attend(qf[j, h], Cf[s_], c_, 1 / 16, dl)
+            assert np.allclose(out[j, h], o, rtol=1e-5, atol=1e-6), (j, h)
+            assert abs(lse[j, h] - l_) < 1e-5 * max(1.0, abs(l_))
+
+
+def pin_attend_constant_v(L):
+    """Rows whose latent part is one vector v: the output is v (the softmax
+    weights sum to one), whatever the scores."""
+    rng = np.random.default_rng(4)
+    T, D, dl = 40, 576, 512
+    v = rng.standard_normal(dl)
+    C = rng.standard_normal((1, T, D))
+    C[0, :, :dl] = v
+    q = bf(rng.standard_normal((1, H, D)) * 3)
+    sel = np.full((1, 64), -1, np.int32)
+    sel[0, :T] = np.arange(T)
+    out, _ = O.mla_attend([0], dl, 64, 1 / 16, q, bf(C), sel, [T], L=L)
+    assert np.allclose(out[0], fl(bf(v))[None, :], rtol=1e-6, atol=1e-7)
+
+
+def pin_attend_two_token_scale(L):
+    """q = 16 e_0, rows e_0 and e_1: z = (1, 0) with scale 1/16, so
+    o = (sigmoid(1), 1 - sigmoid(1), 0, ...) and lse = log(1 + e).  Scale
+    1/sqrt(512) or 1/sqrt(576) would give 0.67 instead of 0.731."""
+    D, dl = 576, 512
+    C = np.zeros((1, 2, D))
+    C[0, 0, 0] = 1
+    C[0, 1, 1] = 1
+    q = np.zeros((1, H, D))
+    q[0, :, 0] = 16
+    sel = np.array([[0, 1]], np.int32)
+    out, lse = O.mla_attend([0], dl, 64, 1 / 16, bf(q), bf(C), sel, [2], L=L)
+    sig = 1 / (1 + math.exp(-1))
+    assert abs(out[0, 0, 0] - 0.7310585786) < 1e-7 and abs(out[0, 0, 0] - sig) < 1e-7
+    assert abs(out[0, 0, 1] - (1 - sig)) < 1e-7
+    assert np.all(out[0, :, 2:] == 0)
+    assert abs(lse[0, 0] - math.log(1 + math.e)) < 1e-6
+
+
+def pin_attend_rope_part_scores(L):
+    """The 64-wide RoPE tail takes part in the score but not in V: with equal
+    latent scores and q = 16 on the first rope column, rows with rope 1 and 0
+    weigh sigmoid(1) and 1 - sigmoid(1); the output carries only latents."""
+    D, dl = 576, 512
+    C = np.zeros((1, 2, D))
+    C[0, 0, 0], C[0, 1, 1] = 1, 1
+    C[0, 0, dl] = 1                 # rope column 0 of row 0
+    C[0, :, dl + 1] = 5             # equal in both rows
+    q = np.zeros((1, H, D))
+    q[0, :, dl] = 16
+    q[0, :, dl + 1] = 2
+    sel = np.array([[0, 1]], np.int32)
+    out, _ = O.mla_attend([0], dl, 64, 1 / 16, bf(q), bf(C), sel, [2], L=L)
+    sig = 1 / (1 + math.exp(-1))
+    assert abs(out[0, 3, 0] - sig) < 1e-7 and abs(out[0, 3, 1] - (1 - sig)) < 1e-7
+
+
+def pin_attend_nope(L):
+    """NoPE rows (d_rope = 0): K = V = the 512-wide latent; float64 numpy."""
+    rng = np.random.default_rng(6)
+    T, dl = 50, 512
+    C = bf(rng.standard_normal((1, T, dl)))
+    q = bf(rng.standard_normal((1, H, dl)))
+    picks = np.array([1, 4, 9, 10, 11, 12, 30, 49], np.int32)
+    sel = np.full((1, 2051), -1, np.int32)
+    sel[0, :8] = picks
+    out, lse = O.mla_attend([0], dl, 0, 1 / 16, q, C, sel, [8], L=L)
+    for h in range(H):
+        o, l_ = brute_attend(fl(q)[0, h], fl(C)[0], picks, 1 / 16, dl)
+        assert np.allclose(out[0, h], o, rtol=1e-5, atol=1e-6)
+        assert abs(lse[0, h] - l_) < 1e-5 * max(1.0, abs(l_))
+
+
+# ---------------------------------------------------------------- fused step
+def pin_decode_is_composition(L):
+    """The fused step equals scores -> top-k -> attention, and a prefill
+    chunk equals one decode per position with n_vis = position + 1."""
+    rng = np.random.default_rng(8)
+    geom = dict(n_heads=H, d_latent=512, d_rope=64, n_idx_heads=HI, d_idx=DI,
+                top_k=16, kpool=1, softmax_scale=1 / 16)
+    T = 40
+    C = bf(rng.standard_normal((1, T, 576)))
+    K = bf(rng.integers(-8, 9, size=(1, T, DI)))
+    nq = 6
+    nvis = np.array([10, 16, 17, 25, 39, 40], np.int32)
+    qseq = np.zeros(nq, np.int32)
+    qi = bf(rng.integers(-8, 9, size=(nq, HI, DI)))
+    w = rng.integers(1, 5, size=(nq, HI)).astype(np.float32)
+    q = bf(rng.standard_normal((nq, H, 576)))
+    sel, cnt, out, lse = O.decode_step(geom, qseq, nvis, qi, w, K, q, C, L=L)
+    s = O.index_scores(qseq, nvis, 1, qi, w, K, L=L)
+    sel2, cnt2 = O.topk(nvis, 1, 16, s, L=L)
+    out2, lse2 = O.mla_attend(qseq, 512, 64, 1 / 16, q, C, sel2, cnt2, L=L)
+    assert np.array_equal(sel, sel2) and np.array_equal(cnt, cnt2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    for j in range(nq):
+        r = brute_select(brute_scores(fl(qi)[j].astype(np.int64), w[j].astype(np.int64),
+                                      fl(K)[0].astype(np.int64), nvis[j]), nvis[j], 1, 16)
+        assert sel[j, :cnt[j]].tolist() == r
+        s1, c1, o1, l1 = O.decode_step(geom, [0], nvis[j:j + 1], qi[j:j + 1], w[j:j + 1],
+                                       K, q[j:j + 1], C, L=L)
+        assert np.array_equal(o1[0], out[j]) and np.array_equal(s1[0], sel[j])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and
+require that the pin suite catches each one.  This measures the pins'
+power: a pin suite that a dropped term, a wrong sign or index, or a
+transposed operand could pass would not be a pin."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle_pins
+from oracle import oracle as O
+
+MUTANTS = [
+    ("relu_dropped", "if (dot > 0.0)\n                    acc +=", "if (1)\n                    acc +="),
+    ("relu_after_weight", "if (dot > 0.0)\n                    acc +=", "if ((double)w[h] * dot > 0.0)\n                    acc +="),
+    ("key_index_shifted", "bf16_value(k[d]);", "bf16_value(k[(d + 1) % d_idx]);"),
+    ("head_stride_wrong", "bf16_value(qi[h * d_idx + d])", "bf16_value(qi[h + d])"),
+    ("rows_off_by_one", "const int64_t rows = q_nvis[q] / kpool;", "const int64_t rows = (q_nvis[q] - 1) / kpool;"),
+    ("seq_ignored_in_scores", "const int64_t seq = q_seq ? q_seq[q] : q;", "const int64_t seq = 0;"),
+    ("ties_to_higher_index", "return (a->r > b->r) - (a->r < b->r);", "return (a->r < b->r) - (a->r > b->r);"),
+    ("ascending_sort_dropped", "qsort(pick, (size_t)keep, sizeof *pick, by_index);", ";"),
+    ("tail_dropped", "for (int64_t t = rows * kpool; t < n_vis; t++)", "for (int64_t t = rows * kpool; t < rows * kpool; t++)"),
+    # ("rows < keep" would be an equivalent mutant: keeping keep of keep rows is dense)
+    ("dense_one_past_budget", "if (rows <= keep) {", "if (rows <= keep + 1) {"),
+    ("keep_one_short", "for (int64_t i = 0; i < keep; i++)\n                pick[i] = all[i].r;",
+     "for (int64_t i = 0; i < keep; i++)\n                pick[i] = all[i + (i == keep - 1)].r;"),
+    ("scale_dropped", "z[i] = (double)scale * dot;", "z[i] = dot;"),
+    ("rope_dropped", "for (int32_t d = 0; d < D; d++)\n                    dot += bf16_value(qh[d])",
+     "for (int32_t d = 0; d < d_latent; d++)\n                    dot += bf16_value(qh[d])"),
+    ("v_from_rope_side", "o[j] += p * bf16_value(c[j]);", "o[j] += p * bf16_value(c[j + d_rope]);"),
+    ("not_normalised", "dst[j] = (float)(o[j] / l);", "dst[j] = (float)o[j];"),
+    ("lse_without_max", "(float)(m + log(l));", "(float)log(l);"),
+    ("query_head_transposed", "q + ((int64_t)qq * n_heads + h) * D;", "q + ((int64_t)h * n_q + qq) * D;"),
+    ("seq_ignored_in_attend", "const int64_t seq = q_seq ? q_seq[qq] : qq;", "const int64_t seq = 0;"),
+    ("pool_expand_wrong", "dst[count++] = (int32_t)(pick[i] * kpool + j);", "dst[count++] = (int32_t)(pick[i] + j);"),
+]
+
+
+def _build_mutant(src: str, name: str, old: str, new: str, tmp: str) -> str:
+    assert old in src, f"mutant {name}: pattern not found"
+    path_c = os.path.join(tmp, f"{name}.c")
+    path_so = os.path.join(tmp, f"lib{name}.so")
+    with open(path_c, "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-o", path_so, path_c, "-lm"])
+    return path_so
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(O.SRC).read()
+    with tempfile.TemporaryDirectory() as tmp:
+        L = O.load(_build_mutant(src, name, old, new, tmp))
+        failed = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(L)
+            except AssertionError:
+                failed.append(pin.__name__)
+            except Exception as e:   # a crash or a refused call also counts
+                failed.append(f"{pin.__name__}: {type(e).__name__}")
+        assert failed, f"mutant {name} passed every pin"
