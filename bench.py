@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused DSA decode step on one MI355X.
+
+Workload: decode at 128K context -- 8 independent sequences of 131,072 cached
+tokens, top-k 2048, 64 absorbed query heads over 576-wide latent rows, a
+32 x 128 indexer with integer-valued keys/queries and weights in [1, 4]
+(synthetic, seeded).  A step is one ``dsa_decode_step`` call over the batch:
+indexer scores of every cached token, exact top-k, sparse absorbed-MLA
+attention, split merge.  Inputs are resident in HBM before timing starts;
+steps rotate over several device replicas of the caches so that no step
+finds its inputs in the 256 MB Infinity Cache left by the previous one.
+
+Prints ONE JSON line.  ``value`` is queries per second; ``roofline`` is the
+dominant kernel (the indexer score kernel): algorithmic bytes per launch over
+its average duration, measured with HIP events on the launch stream;
+``cpu_baseline`` is the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "DSA decode queries/sec at 128K ctx, top-k 2048; achieved HBM GB/s vs peak"
+KERNELS = ["score", "filter", "resolve", "emit", "attend", "merge"]
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per query and per score launch (inputs
+    read once, output written once; intermediates excluded)."""
+    g = w.geom
+    D = g["d_latent"] + g["d_rope"]
+    rows = w.q_nvis.astype("int64") // g["kpool"]
+    keys = rows * g["d_idx"] * 2
+    qi_w = g["n_idx_heads"] * g["d_idx"] * 2 + g["n_idx_heads"] * 4
+    kp, keep = g["kpool"], g["top_k"] // g["kpool"]
+    kept = [int(n) if int(n) // kp <= keep else keep * kp + int(n) % kp for n in w.q_nvis]
+    sel_rows = sum(kept) * D * 2
+    q = w.n_q * g["n_heads"] * D * 2
+    out = w.n_q * g["n_heads"] * g["d_latent"] * 4
+    step = int(keys.sum()) + w.n_q * qi_w + sel_rows + q + out
+    score_launch = int(keys.sum()) + w.n_q * qi_w
+    return step, score_launch
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands, on whole steps of the same workload, repeated
+    until about budget_s seconds of wall time have passed (at most 4 steps)."""
+    from oracle import oracle as O
+    threads = O.max_threads()
+    done, t0 = 0, time.perf_counter()
+    while True:
+        O.decode_step(w.geom, w.q_seq, w.q_nvis, w.idx_q, w.idx_w, w.idx_k, w.q, w.cache)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 4:
+            break
+    return {"value": round(done * w.n_q / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} full step(s) of the same workload ({done * w.n_q} queries), "
+                      f"{el:.1f} s wall on {threads} OpenMP threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="m128k")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=6.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU sharding is a design note, not an implementation)", file=sys.stderr)
+        return 2
+
+    import torch
+    from deepseek_sparse_attention_amd import binding as B
+    from deepseek_sparse_attention_amd import inputs as I
+    from deepseek_sparse_attention_amd.workload import DeviceWorkload
+
+    torch.cuda.set_device(0)
+    B.device_check()
+    t0 = time.perf_counter()
+    w = I.config(args.config, poison_beyond=False)
+    print(f"[bench] {args.config}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    reps = [DeviceWorkload(w) for _ in range(max(1, args.replicas))]
+    R = len(reps)
+    torch.cuda.synchronize()
+    print(f"[bench] {R} device replicas resident", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        reps[i % R].decode_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        reps[i % R].decode_step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    qps = w.n_q / (ms_step * 1e-3)
+    step_bytes, score_bytes = algorithmic_bytes(w)
+    print(f"[bench] {ms_step * 1e3:.1f} us/step, wall {wall * 1e3 / args.steps:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    # ---- per-kernel durations: events recorded by the library around each
+    # kernel of the same fused step, over a second pass of the same length
+    n_k = len(KERNELS) + 1
+    n_rep = min(args.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k)] for _ in range(n_rep)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(n_rep):
+        B.set_timing_events(evs[i])
+        reps[i % R].decode_step()
+    B.set_timing_events(None)
+    torch.cuda.synchronize()
+    names = KERNELS
+    per = {k: 0.0 for k in names}
+    for row in evs:
+        for j, k in enumerate(names):
+            per[k] += row[j].elapsed_time(row[j + 1]) * 1e3 / n_rep
+    score_us = per["score"]
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": _workload_name(w), "batch": w.n_q, "context": int(w.q_nvis.max()),
+                   "top_k": w.geom["top_k"], "replicas": R},
+        "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in per.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_score", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": score_bytes},
+    }
+    if not args.no_cpu_baseline:
+        del reps
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _workload_name(w) -> str:
+    g = w.geom
+    return (f"{w.name}: decode, {w.n_q} sequences x {int(w.q_nvis.max())} cached tokens, top-k {g['top_k']}, "
+            f"kpool {g['kpool']}, {g['n_heads']} heads x {g['d_latent'] + g['d_rope']} latent rows, "
+            f"indexer {g['n_idx_heads']}x{g['d_idx']}")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

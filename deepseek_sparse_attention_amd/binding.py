@@ -1,0 +1,154 @@
+"""Thin ctypes binding of ``libdsa.so`` (the C ABI in ``include/dsa.h``).
+
+Argument marshalling only: torch supplies device memory and the current
+stream, every step runs in the HIP kernels behind the C ABI.  There is no
+fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_DEVICE, DSA_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("n_idx_heads", ctypes.c_int32), ("d_idx", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("kpool", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("n_seq", ctypes.c_int32), ("q_seq", ctypes.c_void_p),
+                ("q_nvis", ctypes.c_void_p), ("max_nvis", ctypes.c_int64), ("q_per_seq_hint", ctypes.c_int32)]
+
+
+EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
+           "dsa_decode_step", "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events")
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m deepseek_sparse_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    G, B = ctypes.POINTER(Geometry), ctypes.POINTER(Batch)
+    sig = {
+        "dsa_workspace_bytes": (sz, [G, i32, i64]),
+        "dsa_workspace_init": (ctypes.c_int, [P, sz, P]),
+        "dsa_index_scores": (ctypes.c_int, [G, B, P, P, P, i64, P, i64, P]),
+        "dsa_topk": (ctypes.c_int, [G, B, P, i64, P, i32, P, P, sz, P]),
+        "dsa_mla_attend": (ctypes.c_int, [G, B, P, P, i64, P, i32, P, P, P, P, sz, P]),
+        "dsa_decode_step": (ctypes.c_int, [G, B, P, P, P, i64, P, P, i64, P, i32, P, P, P, P, sz, P]),
+        "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "dsa_last_error": (ctypes.c_char_p, []),
+        "dsa_device_check": (ctypes.c_int, []),
+        "dsa_set_timing_events": (ctypes.c_int, [P, i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+_lib = load_library()
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        detail = _lib.dsa_last_error().decode()
+        super().__init__(f"{what}: {_lib.dsa_status_str(status).decode()} ({status}): {detail}")
+
+
+def _check(status: int, what: str) -> None:
+    if status != DSA_OK:
+        raise DSAError(status, what)
+
+
+def geometry(geom: dict) -> Geometry:
+    return Geometry(geom["n_heads"], geom["d_latent"], geom["d_rope"], geom["n_idx_heads"], geom["d_idx"],
+                    geom["top_k"], geom["kpool"], float(geom["softmax_scale"]))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def batch(q_seq: torch.Tensor | None, q_nvis: torch.Tensor, max_nvis: int, n_seq: int,
+          q_per_seq_hint: int = 0) -> Batch:
+    """The C struct holds raw device pointers; the returned object keeps the
+    two tensors alive for as long as it lives."""
+    for t in (q_seq, q_nvis):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("q_seq / q_nvis must be contiguous int32 device tensors")
+    b = Batch(int(q_nvis.shape[0]), int(n_seq), _ptr(q_seq), _ptr(q_nvis), int(max_nvis), int(q_per_seq_hint))
+    b._keep = (q_seq, q_nvis)
+    return b
+
+
+def workspace_bytes(geom: dict, n_q: int, max_nvis: int) -> int:
+    return int(_lib.dsa_workspace_bytes(ctypes.byref(geometry(geom)), n_q, max_nvis))
+
+
+def new_workspace(geom: dict, n_q: int, max_nvis: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (uint8) of the size the library asks for."""
+    n = workspace_bytes(geom, n_q, max_nvis)
+    if n == 0:
+        raise DSAError(DSA_ERR_UNSUPPORTED, "workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(_lib.dsa_workspace_init(_ptr(ws), n, _stream(None)), "dsa_workspace_init")
+    return ws
+
+
+def device_check() -> None:
+    _check(_lib.dsa_device_check(), "dsa_device_check")
+
+
+def index_scores(geom: dict, b: Batch, idx_q, idx_w, idx_k, key_seq_stride: int, scores, score_ld: int,
+                 stream=None) -> None:
+    _check(_lib.dsa_index_scores(ctypes.byref(geometry(geom)), ctypes.byref(b), _ptr(idx_q), _ptr(idx_w),
+                                 _ptr(idx_k), int(key_seq_stride), _ptr(scores), int(score_ld), _stream(stream)),
+           "dsa_index_scores")
+
+
+def topk(geom: dict, b: Batch, scores, score_ld: int, sel, sel_ld: int, sel_count, ws, stream=None) -> None:
+    _check(_lib.dsa_topk(ctypes.byref(geometry(geom)), ctypes.byref(b), _ptr(scores), int(score_ld), _ptr(sel),
+                         int(sel_ld), _ptr(sel_count), _ptr(ws), ws.numel() if ws is not None else 0,
+                         _stream(stream)), "dsa_topk")
+
+
+def mla_attend(geom: dict, b: Batch, q, cache, cache_seq_stride: int, sel, sel_ld: int, sel_count, out, lse, ws,
+               stream=None) -> None:
+    _check(_lib.dsa_mla_attend(ctypes.byref(geometry(geom)), ctypes.byref(b), _ptr(q), _ptr(cache),
+                               int(cache_seq_stride), _ptr(sel), int(sel_ld), _ptr(sel_count), _ptr(out), _ptr(lse),
+                               _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "dsa_mla_attend")
+
+
+def decode_step(geom: dict, b: Batch, idx_q, idx_w, idx_k, key_seq_stride: int, q, cache, cache_seq_stride: int,
+                sel, sel_ld: int, sel_count, out, lse, ws, stream=None) -> None:
+    _check(_lib.dsa_decode_step(ctypes.byref(geometry(geom)), ctypes.byref(b), _ptr(idx_q), _ptr(idx_w),
+                                _ptr(idx_k), int(key_seq_stride), _ptr(q), _ptr(cache), int(cache_seq_stride),
+                                _ptr(sel), int(sel_ld), _ptr(sel_count), _ptr(out), _ptr(lse), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream)), "dsa_decode_step")
+
+
+def set_timing_events(events) -> None:
+    """events: a list of torch.cuda.Event(enable_timing=True), or None to stop.
+    The library records them around each kernel of dsa_decode_step."""
+    if not events:
+        _lib.dsa_set_timing_events(None, 0)
+        set_timing_events._keep = None
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    set_timing_events._keep = (arr, events)
+    _check(_lib.dsa_set_timing_events(ctypes.cast(arr, ctypes.c_void_p), len(events)), "dsa_set_timing_events")

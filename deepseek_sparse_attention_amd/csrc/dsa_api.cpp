@@ -1,0 +1,355 @@
+// dsa_api.cpp -- host side of the C ABI declared in include/dsa.h:
+// argument validation, workspace plan, path choice and kernel enqueue on
+// the caller's stream.  Nothing here allocates device memory or waits for
+// the device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <string>
+
+#include "dsa.h"
+#include "dsa_plan.h"
+
+#include "dsa_args.h"
+
+namespace dsa {
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st);
+hipError_t launch_hist(const Args &a, hipStream_t st);
+hipError_t launch_filter(const Args &a, hipStream_t st);
+hipError_t launch_resolve(const Args &a, hipStream_t st);
+hipError_t launch_emit(const Args &a, hipStream_t st);
+hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
+}  // namespace dsa
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t *g_events = nullptr;
+thread_local int32_t g_n_events = 0;
+
+// Records the next timing event of this call, if instrumentation is on.
+struct Timer {
+    hipStream_t st;
+    int32_t next = 0;
+    explicit Timer(hipStream_t s) : st(s) { tick(); }
+    void tick() {
+        if (g_events && next < g_n_events) (void)hipEventRecord(g_events[next++], st);
+    }
+};
+
+int fail(int status, const std::string &msg) {
+    g_last_error = msg;
+    return status;
+}
+
+// Per-device result of the architecture check (0 unknown, 1 gfx950, 2 other).
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(DSA_ERR_DEVICE, "no current HIP device");
+    if (dev < 64) {
+        int s = g_dev_ok[dev].load(std::memory_order_acquire);
+        if (s == 1) return DSA_OK;
+        if (s == 2) return fail(DSA_ERR_DEVICE, "current device is not a gfx950");
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(DSA_ERR_DEVICE, "hipGetDeviceProperties failed");
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+    if (!ok) return fail(DSA_ERR_DEVICE, std::string("current device is ") + prop.gcnArchName + ", not gfx950");
+    return DSA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_geometry(const dsa_geometry *g) {
+    if (!g) return fail(DSA_ERR_ARG, "geometry is NULL");
+    if (g->n_heads != dsa::kHeads || g->d_latent != dsa::kLatent || g->n_idx_heads != dsa::kIdxHeads ||
+        g->d_idx != dsa::kIdxDim)
+        return fail(DSA_ERR_UNSUPPORTED, "only n_heads 64, d_latent 512, n_idx_heads 32, d_idx 128 are implemented");
+    if (g->d_rope != 64 && g->d_rope != 0) return fail(DSA_ERR_UNSUPPORTED, "d_rope must be 64 or 0");
+    if (g->kpool != 1 && g->kpool != 4) return fail(DSA_ERR_UNSUPPORTED, "kpool must be 1 or 4");
+    if (g->top_k < 1 || g->top_k > dsa::kMaxTopK || g->top_k % g->kpool != 0)
+        return fail(DSA_ERR_UNSUPPORTED, "top_k must be in [1, 4096] and a multiple of kpool");
+    if (!(std::isfinite(g->softmax_scale) && g->softmax_scale > 0.f))
+        return fail(DSA_ERR_UNSUPPORTED, "softmax_scale must be finite and positive");
+    return DSA_OK;
+}
+
+int check_batch(const dsa_batch *b) {
+    if (!b) return fail(DSA_ERR_ARG, "batch is NULL");
+    if (b->n_q < 1) return fail(DSA_ERR_ARG, "n_q must be >= 1");
+    if (b->n_seq < 1) return fail(DSA_ERR_ARG, "n_seq must be >= 1");
+    if (!b->q_nvis) return fail(DSA_ERR_ARG, "q_nvis is NULL");
+    if (!b->q_seq && b->n_q > b->n_seq) return fail(DSA_ERR_ARG, "q_seq NULL needs n_q <= n_seq");
+    if (b->max_nvis < 1 || b->max_nvis > (int64_t)INT32_MAX) return fail(DSA_ERR_ARG, "max_nvis must be in [1, 2^31)");
+    if (!aligned16(b->q_nvis) || (b->q_seq && !aligned16(b->q_seq)))
+        return fail(DSA_ERR_ARG, "q_seq / q_nvis must be 16-byte aligned");
+    return DSA_OK;
+}
+
+#define DSA_TRY(expr)                         \
+    do {                                      \
+        int _s = (expr);                      \
+        if (_s != DSA_OK) return _s;          \
+    } while (0)
+
+bool test_fail_launch() {
+    const char *e = std::getenv("DSA_TEST_FAIL_LAUNCH");
+    return e && e[0] == '1';
+}
+
+dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p) {
+    dsa::Args a;
+    std::memset(&a, 0, sizeof a);
+    a.n_q = b->n_q;
+    a.n_seq = b->n_seq;
+    a.q_seq = b->q_seq;
+    a.q_nvis = b->q_nvis;
+    a.max_nvis = b->max_nvis;
+    a.kpool = g->kpool;
+    a.top_k = g->top_k;
+    a.keep = p.keep;
+    a.D = p.D;
+    a.scale_log2 = g->softmax_scale * 1.4426950408889634f;
+    a.chunk = p.chunk;
+    a.n_chunks = p.n_chunks;
+    a.cand_cap = p.cand_cap;
+    a.split_rows = p.split_rows;
+    a.n_split = p.n_split;
+    a.score_tile = p.score_tile;
+    return a;
+}
+
+void bind_workspace(dsa::Args &a, const dsa::Plan &p, void *ws) {
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    a.hist = reinterpret_cast<uint32_t *>(w + p.off_hist);
+    a.cand_n = reinterpret_cast<uint32_t *>(w + p.off_candn);
+    a.done = reinterpret_cast<uint32_t *>(w + p.off_done);
+    a.thr = reinterpret_cast<dsa::Threshold *>(w + p.off_thr);
+    a.chunks = reinterpret_cast<dsa::ChunkInfo *>(w + p.off_chunk);
+    a.cand = reinterpret_cast<uint64_t *>(w + p.off_cand);
+    a.pacc = reinterpret_cast<float *>(w + p.off_pacc);
+    a.pml = reinterpret_cast<float *>(w + p.off_pml);
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(DSA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+    return DSA_OK;
+}
+
+int check_ws(const dsa::Plan &p, const void *ws, size_t ws_bytes) {
+    if (!ws) return fail(DSA_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(DSA_ERR_ARG, "workspace must be 16-byte aligned");
+    if (ws_bytes < p.total)
+        return fail(DSA_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                           std::to_string(p.total));
+    return DSA_OK;
+}
+
+template <class F>
+int guarded(F &&f) {
+    try {
+        g_last_error.clear();
+        return f();
+    } catch (...) {
+        return fail(DSA_ERR_ARG, "unexpected host exception");
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_status_str(int s) {
+    switch (s) {
+        case DSA_OK: return "ok";
+        case DSA_ERR_ARG: return "invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "unsupported geometry";
+        case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSA_ERR_DEVICE: return "current device is not a gfx950";
+        case DSA_ERR_LAUNCH: return "kernel launch refused";
+        default: return "unknown status";
+    }
+}
+
+const char *dsa_last_error(void) { return g_last_error.c_str(); }
+
+int dsa_set_timing_events(hipEvent_t *events, int32_t n_events) {
+    g_events = (events && n_events > 0) ? events : nullptr;
+    g_n_events = g_events ? n_events : 0;
+    return DSA_OK;
+}
+
+int dsa_device_check(void) {
+    return guarded([&] { return check_device(); });
+}
+
+size_t dsa_workspace_bytes(const dsa_geometry *g, int32_t n_q, int64_t max_nvis) {
+    if (check_geometry(g) != DSA_OK || n_q < 1 || max_nvis < 1 || max_nvis > (int64_t)INT32_MAX) return 0;
+    return dsa::make_plan(g->kpool, g->top_k, g->d_rope, n_q, max_nvis).total;
+}
+
+int dsa_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        if (!ws || !aligned16(ws)) return fail(DSA_ERR_ARG, "workspace NULL or misaligned");
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        return launched(dsa::launch_fill_zero(ws, ws_bytes, stream), "fill");
+    });
+}
+
+int dsa_index_scores(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *idx_q, const float *idx_w,
+                     const dsa_bf16 *idx_k, int64_t key_seq_stride, float *scores, int64_t score_ld,
+                     hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        DSA_TRY(check_geometry(g));
+        DSA_TRY(check_batch(b));
+        if (!idx_q || !idx_w || !idx_k || !scores) return fail(DSA_ERR_ARG, "NULL tensor pointer");
+        if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(idx_k) || !aligned16(scores))
+            return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
+        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
+        if (score_ld < p.max_rows) return fail(DSA_ERR_ARG, "score_ld < max_nvis / kpool");
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::Args a = base_args(g, b, p);
+        a.idx_q = idx_q;
+        a.idx_w = idx_w;
+        a.idx_k = idx_k;
+        a.key_stride = key_seq_stride;
+        a.scores = scores;
+        a.score_ld = score_ld;
+        a.fused = 0;
+        return launched(dsa::launch_score(a, p.max_rows, stream), "score");
+    });
+}
+
+int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int64_t score_ld, int32_t *sel,
+             int32_t sel_ld, int32_t *sel_count, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        DSA_TRY(check_geometry(g));
+        DSA_TRY(check_batch(b));
+        if (!scores || !sel || !sel_count) return fail(DSA_ERR_ARG, "NULL tensor pointer");
+        if (!aligned16(scores) || !aligned16(sel) || !aligned16(sel_count))
+            return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
+        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        if (score_ld < p.max_rows) return fail(DSA_ERR_ARG, "score_ld < max_nvis / kpool");
+        if (sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
+        DSA_TRY(check_ws(p, ws, ws_bytes));
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::Args a = base_args(g, b, p);
+        bind_workspace(a, p, ws);
+        a.scores_in = scores;
+        a.score_ld = score_ld;
+        a.sel = sel;
+        a.sel_ld = sel_ld;
+        a.sel_count = sel_count;
+        DSA_TRY(launched(dsa::launch_hist(a, stream), "hist"));
+        DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
+        DSA_TRY(launched(dsa::launch_resolve(a, stream), "resolve"));
+        return launched(dsa::launch_emit(a, stream), "emit");
+    });
+}
+
+int dsa_mla_attend(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *q, const dsa_bf16 *cache,
+                   int64_t cache_seq_stride, const int32_t *sel, int32_t sel_ld, const int32_t *sel_count,
+                   float *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        DSA_TRY(check_geometry(g));
+        DSA_TRY(check_batch(b));
+        if (!q || !cache || !sel || !sel_count || !out) return fail(DSA_ERR_ARG, "NULL tensor pointer");
+        if (!aligned16(q) || !aligned16(cache) || !aligned16(sel) || !aligned16(sel_count) || !aligned16(out) ||
+            (lse && !aligned16(lse)))
+            return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
+        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
+        if (sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
+        DSA_TRY(check_ws(p, ws, ws_bytes));
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::Args a = base_args(g, b, p);
+        bind_workspace(a, p, ws);
+        a.q = q;
+        a.cache = cache;
+        a.cache_stride = cache_seq_stride;
+        a.sel = const_cast<int32_t *>(sel);
+        a.sel_ld = sel_ld;
+        a.sel_count = const_cast<int32_t *>(sel_count);
+        a.out = out;
+        a.lse = lse;
+        return launched(dsa::launch_attend(a, stream), "attend");
+    });
+}
+
+int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *idx_q, const float *idx_w,
+                    const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q, const dsa_bf16 *cache,
+                    int64_t cache_seq_stride, int32_t *sel, int32_t sel_ld, int32_t *sel_count, float *out,
+                    float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        DSA_TRY(check_geometry(g));
+        DSA_TRY(check_batch(b));
+        if (!idx_q || !idx_w || !idx_k || !q || !cache || !out) return fail(DSA_ERR_ARG, "NULL tensor pointer");
+        if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(idx_k) || !aligned16(q) || !aligned16(cache) ||
+            !aligned16(out) || (lse && !aligned16(lse)) || (sel && !aligned16(sel)) ||
+            (sel_count && !aligned16(sel_count)))
+            return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
+        if ((sel == nullptr) != (sel_count == nullptr)) return fail(DSA_ERR_ARG, "sel and sel_count go together");
+        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
+        if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
+        if (sel && sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
+        DSA_TRY(check_ws(p, ws, ws_bytes));
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::Args a = base_args(g, b, p);
+        bind_workspace(a, p, ws);
+        uint8_t *w = static_cast<uint8_t *>(ws);
+        a.idx_q = idx_q;
+        a.idx_w = idx_w;
+        a.idx_k = idx_k;
+        a.key_stride = key_seq_stride;
+        a.scores = reinterpret_cast<float *>(w + p.off_scores);
+        a.scores_in = a.scores;
+        a.score_ld = p.score_ld;
+        a.q = q;
+        a.cache = cache;
+        a.cache_stride = cache_seq_stride;
+        if (sel) {
+            a.sel = sel;
+            a.sel_ld = sel_ld;
+            a.sel_count = sel_count;
+        } else {
+            a.sel = reinterpret_cast<int32_t *>(w + p.off_sel);
+            a.sel_ld = p.sel_max;
+            a.sel_count = reinterpret_cast<int32_t *>(w + p.off_cnt);
+        }
+        a.out = out;
+        a.lse = lse;
+        a.fused = 1;
+        Timer tm(stream);
+        DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream), "score"));
+        tm.tick();
+        DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
+        tm.tick();
+        DSA_TRY(launched(dsa::launch_resolve(a, stream), "resolve"));
+        tm.tick();
+        DSA_TRY(launched(dsa::launch_emit(a, stream), "emit"));
+        tm.tick();
+        DSA_TRY(launched(dsa::launch_attend(a, stream, [&] { tm.tick(); }), "attend"));
+        tm.tick();
+        return (int)DSA_OK;
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// dsa_args.h -- argument block passed by value to every DSA kernel.
+#pragma once
+
+#include <stdint.h>
+
+#include "dsa_plan.h"
+
+namespace dsa {
+
+struct Args {
+    // batch
+    int32_t n_q, n_seq;
+    const int32_t *q_seq, *q_nvis;
+    int64_t max_nvis;
+    // geometry
+    int32_t kpool, top_k, keep, D;
+    float scale_log2;     // softmax_scale * log2(e)
+    // tensors
+    const uint16_t *idx_q;
+    const float *idx_w;
+    const uint16_t *idx_k;
+    int64_t key_stride;
+    const uint16_t *q, *cache;
+    int64_t cache_stride;
+    const float *scores_in;
+    float *scores;
+    int64_t score_ld;
+    int32_t *sel;
+    int32_t sel_ld;
+    int32_t *sel_count;
+    float *out, *lse;
+    // workspace
+    uint32_t *hist, *cand_n, *done;
+    Threshold *thr;
+    ChunkInfo *chunks;
+    uint64_t *cand;
+    float *pacc, *pml;
+    // plan
+    int32_t chunk, n_chunks, cand_cap, split_rows, n_split, score_tile;
+    int32_t fused;        // 1: dense queries are not scored, histogram accumulated
+};
+
+}  // namespace dsa

@@ -1,0 +1,842 @@
+// dsa_kernels.hip -- HIP kernels of the DeepSeek Sparse Attention decode hot
+// path for CDNA4 (gfx950, wave64, MFMA 16x16x32 bf16, LDS transpose reads).
+//
+// Steps and the pages that define them:
+//  * indexer scores: "GLM 5.2 in pure C", section "The Lightning Indexer:
+//    Sparse Attention When It Helps" (per-head rectified dot product, then a
+//    weighted sum over the 32 heads of TensorSharp2's table "The block");
+//  * top-k: same section (keep the best index_topk rows; all of them when
+//    fewer are visible, TensorSharp2 "The sparse-attention path"); ties go
+//    to the lower index ("GLM-5.3-Flash on WASTE", "k-pool flavour");
+//  * pools: WASTE "k-pool flavour" and TensorSharp2 "GLM-5.3-Flash
+//    (glm5next)": keep top_k/4 pools, expand to tokens, add the unpooled tail;
+//  * attention: "GLM 5.2 in pure C", section "Attention: Multi head Latent
+//    Attention With a Tiny KV Cache" (absorbed query dotted with the latent
+//    and rope parts, scaled, softmax, latents pooled); scale 1/16 from
+//    TensorSharp2 "The block".
+//
+// Design (gfx950): the indexer is a [32 x 128] x [128 x rows] product per
+// query, issued on MFMA with the key rows streamed straight from HBM into the
+// B operand; its epilogue applies ReLU and the head weights and feeds a
+// 2048-bin histogram of the scores' order keys.  Top-k is an exact radix
+// select: the histogram fixes the threshold bucket, one pass collects that
+// bucket's candidates, the last work-group of each query resolves the exact
+// threshold and each chunk's output offset, and a final pass emits indices
+// in ascending order.  Attention gathers the selected rows into LDS, computes
+// S^T = C Q^T on MFMA, keeps an online softmax in fp32, and computes
+// O^T = V^T P^T on MFMA with V read through ds_read_b64_tr_b16 and P split
+// into two bf16 halves (hi + lo) so that P carries ~16 mantissa bits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <functional>
+
+#include "dsa_args.h"
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ---------------------------------------------------------------- helpers
+// Order-preserving unsigned image of a float; -0 ranks as +0.
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct QInfo {
+    int32_t seq, nvis, rows, mode;   // mode 0 dense, 1 sparse, 2 invalid
+};
+
+__device__ __forceinline__ QInfo query_info(const Args &a, int q) {
+    QInfo r;
+    r.seq = a.q_seq ? a.q_seq[q] : q;
+    r.nvis = a.q_nvis[q];
+    if (r.seq < 0 || r.seq >= a.n_seq || r.nvis < 1 || (int64_t)r.nvis > a.max_nvis) {
+        r.mode = 2;
+        r.rows = 0;
+        return r;
+    }
+    r.rows = r.nvis / a.kpool;
+    r.mode = (r.rows <= a.keep) ? 0 : 1;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Exclusive prefix sum over a 256-thread block; smem needs 4 words.
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t *smem, uint32_t &total) {
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= (uint32_t)o) x += y;
+    }
+    if (lane == 63) smem[w] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    for (uint32_t i = 0; i < w; i++) base += smem[i];
+    total = smem[0] + smem[1] + smem[2] + smem[3];
+    __syncthreads();
+    return base + x - v;
+}
+
+__device__ uint32_t block_sum(uint32_t v, uint32_t *smem) {
+    uint32_t total;
+    block_excl_scan(v, smem, total);
+    return total;
+}
+
+// Radix step: with hist[0..nbins) of the items still in play and `need` of
+// them still to take from the top, find the bin b holding the need-th
+// largest: suffix(b) >= need > suffix(b+1).  Returns b, sets above =
+// suffix(b+1).  nbins is 2048 or 1024; 256 threads.
+__device__ uint32_t find_bucket(const uint32_t *hist, int nbins, uint32_t need, uint32_t *smem,
+                                uint32_t *res, uint32_t &above) {
+    const int per = nbins / 256;
+    // thread t owns bins [nbins - per*(t+1), nbins - per*t): descending order
+    const int hi = nbins - per * (int)threadIdx.x;
+    uint32_t s = 0;
+    for (int i = 1; i <= per; i++) s += hist[hi - i];
+    uint32_t total;
+    uint32_t before = block_excl_scan(s, smem, total);   // items in higher bins
+    if (before < need && before + s >= need) {
+        uint32_t run = before;
+        for (int i = 1; i <= per; i++) {
+            const uint32_t c = hist[hi - i];
+            if (run + c >= need) {
+                res[0] = (uint32_t)(hi - i);
+                res[1] = run;
+                break;
+            }
+            run += c;
+        }
+    }
+    __syncthreads();
+    above = res[1];
+    const uint32_t b = res[0];
+    __syncthreads();
+    return b;
+}
+
+// ---------------------------------------------------------------- workspace
+__global__ void k_fill_zero(uint32_t *p, size_t n_words) {
+    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n_words; i += stride) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------- scores
+// grid (tiles, n_q), 256 threads.  Wave w of a work-group takes 64-row steps
+// t0 + 64 (w + 4 i).  Per 16 rows: A = idx_q (heads x d, two 16-head blocks,
+// from registers), B = keys^T (d x rows) loaded straight from memory in the
+// MFMA operand layout: lane (g = l/16, n = l%16) holds row n, d in
+// [32 s + 8 g, +8) for k-step s.  D[head][row] lands as lane (g, n) holding
+// heads 4g + r (+16) of row n.
+__global__ __launch_bounds__(256) void k_score(Args a) {
+    __shared__ uint32_t lhist[kHistBins];
+    const int q = blockIdx.y;
+    const QInfo qi = query_info(a, q);
+    if (qi.mode == 2) return;
+    if (a.fused && qi.mode == 0) return;
+    const int64_t t0 = (int64_t)blockIdx.x * a.score_tile;
+    const int64_t rows = qi.rows;
+    if (t0 >= rows) return;
+    const bool hist = a.fused != 0;
+    if (hist) {
+        for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+        __syncthreads();
+    }
+    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+
+    bf16x8 qa[2][4];
+    float wt[2][4];
+    const uint16_t *qip = a.idx_q + (size_t)q * kIdxHeads * kIdxDim;
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            u32x4 v = *(const u32x4 *)(qip + (16 * mb + n) * kIdxDim + 32 * s + 8 * g);
+            qa[mb][s] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)q * kIdxHeads + 16 * mb + 4 * g + r];
+    }
+    const uint16_t *K = a.idx_k + (size_t)qi.seq * a.key_stride * kIdxDim;
+    float *srow = a.scores + (size_t)q * a.score_ld;
+    const int st_mine = 2 * (g & 1) + (g >> 1);
+
+    for (int64_t base = t0 + 64 * w; base < t0 + a.score_tile && base < rows; base += 256) {
+        u32x4 v[4][4];
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            int64_t r = base + 16 * st + n;
+            r = r < rows ? r : rows - 1;
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+                v[st][s] = __builtin_nontemporal_load((const u32x4 *)(K + r * kIdxDim + 32 * s + 8 * g));
+        }
+        float p[4];
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                bf16x8 b = __builtin_bit_cast(bf16x8, v[st][s]);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], b, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], b, acc1, 0, 0, 0);
+            }
+            float x = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                x += wt[0][r] * fmaxf(acc0[r], 0.f);
+                x += wt[1][r] * fmaxf(acc1[r], 0.f);
+            }
+            p[st] = x;
+        }
+        // sum the four lane groups; each lane keeps one of the four 16-row steps
+        const bool b0 = g & 1, b1 = (g >> 1) & 1;
+        const float send0 = b0 ? p[0] : p[2], send1 = b0 ? p[1] : p[3];
+        const float keep0 = b0 ? p[2] : p[0], keep1 = b0 ? p[3] : p[1];
+        const float q0 = keep0 + __shfl_xor(send0, 16, 64);
+        const float q1 = keep1 + __shfl_xor(send1, 16, 64);
+        const float score = (b1 ? q1 : q0) + __shfl_xor(b1 ? q0 : q1, 32, 64);
+        const int64_t row = base + 16 * st_mine + n;
+        if (row < rows) {
+            srow[row] = score;
+            if (hist) atomicAdd(&lhist[order_key(score) >> 21], 1u);
+        }
+    }
+    if (hist) {
+        __syncthreads();
+        uint32_t *gh = a.hist + (size_t)q * kHistBins;
+        for (int i = threadIdx.x; i < kHistBins; i += 256)
+            if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
+    }
+}
+
+// Histogram of caller-provided scores (the standalone top-k entry point).
+// grid (n_chunks, n_q), 256 threads.
+__global__ __launch_bounds__(256) void k_hist(Args a) {
+    __shared__ uint32_t lhist[kHistBins];
+    const int q = blockIdx.y, c = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    if (qi.mode != 1) return;
+    const int64_t r0 = (int64_t)c * a.chunk;
+    if (r0 >= qi.rows) return;
+    const int64_t r1 = r0 + a.chunk < qi.rows ? r0 + a.chunk : qi.rows;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+    __syncthreads();
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) atomicAdd(&lhist[order_key(s[r]) >> 21], 1u);
+    __syncthreads();
+    uint32_t *gh = a.hist + (size_t)q * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256)
+        if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
+}
+
+// ---------------------------------------------------------------- top-k
+// Pass over each chunk: count rows above the threshold bucket, collect the
+// bucket's rows as candidates.  The last chunk of a query to finish resolves
+// the exact threshold and the per-chunk output offsets, then restores the
+// query's histogram and counters to zero.  grid (n_chunks, n_q), 256 threads.
+constexpr int kStash = 4096;     // rows of the level-2 bucket kept in LDS
+
+struct ResolveShared {
+    uint32_t hist[kHistBins];     // first digit, then reused for the second
+    uint32_t h3[1024];            // third digit
+    uint32_t gtc[kMaxChunks];     // per chunk: bucket rows above the threshold
+    uint32_t eqc[kMaxChunks];     // per chunk: rows equal to the threshold
+    uint64_t stash[kStash];       // (key, row) of the level-2 bucket
+    uint32_t scan[8];
+    uint32_t res[4];
+    uint32_t stash_n;
+};
+
+// Candidates (order key, row) of the first-digit bucket, read in rounds of
+// 16 per thread so that each round costs one memory round trip.  From the
+// candidate list when it fits, else by re-deriving them from the scores.
+template <class F>
+__device__ __forceinline__ void for_bucket_rows(const Args &a, bool from_list, const uint64_t *cand, uint32_t nc,
+                                                const float *s, int64_t rows, uint32_t b1, F &&f) {
+    if (from_list) {
+        for (uint32_t base = 0; base < nc; base += 16 * 256) {
+            uint64_t e[16];
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const uint32_t i = base + 256 * j + threadIdx.x;
+                e[j] = i < nc ? cand[i] : 0ull;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; j++)
+                if (e[j]) f((uint32_t)(e[j] >> 32), (uint32_t)e[j]);
+        }
+    } else {
+        for (int64_t base = 0; base < rows; base += 16 * 256) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int64_t r = base + 256 * j + threadIdx.x;
+                v[j] = r < rows ? s[r] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int64_t r = base + 256 * j + threadIdx.x;
+                const uint32_t key = order_key(v[j]);
+                if (r < rows && (key >> 21) == b1) f(key, (uint32_t)r);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_filter(Args a) {
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t scan[8];
+    __shared__ uint32_t res[4];
+    const int q = blockIdx.y, c = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    if (qi.mode != 1) return;
+    const int64_t rows = qi.rows;
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    if (c >= nch) return;
+    const uint32_t keep = (uint32_t)a.keep;
+    uint32_t *gh = a.hist + (size_t)q * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) hist[i] = gh[i];
+    __syncthreads();
+    uint32_t n_gt1;
+    const uint32_t b1 = find_bucket(hist, kHistBins, keep, scan, res, n_gt1);
+
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const int64_t r0 = (int64_t)c * a.chunk;
+    const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+    uint64_t *cand = a.cand + (size_t)q * a.cand_cap;
+    uint32_t gt = 0;
+    // blocks of 2048 rows, 8 per thread; one atomic per block reserves the
+    // block's candidate slots (same-address atomics from every work-group
+    // would serialize)
+    for (int64_t sb = r0; sb < r1; sb += 2048) {
+        uint32_t keys[8];
+        uint32_t n_c = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t r = sb + 256 * i + threadIdx.x;
+            uint32_t key = 0;
+            bool is_c = false;
+            if (r < r1) {
+                key = order_key(s[r]);
+                const uint32_t d1 = key >> 21;
+                gt += d1 > b1 ? 1u : 0u;
+                is_c = d1 == b1;
+            }
+            keys[i] = is_c ? key : 0u;
+            n_c += is_c ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t excl = block_excl_scan(n_c, scan, tot);
+        if (tot == 0) continue;
+        if (threadIdx.x == 0) res[2] = atomicAdd(&a.cand_n[q], tot);
+        __syncthreads();
+        uint32_t pos = res[2] + excl;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (!keys[i]) continue;      // order keys of real scores are never 0
+            const int64_t r = sb + 256 * i + threadIdx.x;
+            if (pos < (uint32_t)a.cand_cap) cand[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)r;
+            pos++;
+        }
+    }
+    gt = block_sum(gt, scan);
+    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
+    if (threadIdx.x == 0) ci[c].gt = gt;
+}
+
+// Exact threshold of each sparse query from its first-digit histogram and
+// the collected candidates: two more radix digits, then each chunk's output
+// offset and its share of the rows equal to the threshold (lowest chunks
+// first).  Restores the query's histogram and counter to zero.  grid (n_q),
+// 256 threads.
+__global__ __launch_bounds__(256) void k_resolve(Args a) {
+    __shared__ ResolveShared sh;
+    const int q = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    if (qi.mode != 1) return;
+    const int64_t rows = qi.rows;
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    const uint32_t keep = (uint32_t)a.keep;
+    uint32_t *gh = a.hist + (size_t)q * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) sh.hist[i] = gh[i];
+    __syncthreads();
+    uint32_t n_gt1;
+    const uint32_t b1 = find_bucket(sh.hist, kHistBins, keep, sh.scan, sh.res, n_gt1);
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const uint64_t *cand = a.cand + (size_t)q * a.cand_cap;
+    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
+    const uint32_t nc = a.cand_n[q];
+    const bool from_list = nc <= (uint32_t)a.cand_cap;
+    const uint32_t need1 = keep - n_gt1;
+    const uint32_t ch = (uint32_t)a.chunk;
+    // pass A: second digit (key bits 20..10) over the bucket
+    uint32_t *h2 = sh.hist;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h2[i] = 0;
+    for (int i = threadIdx.x; i < nch; i += 256) {
+        sh.gtc[i] = 0;
+        sh.eqc[i] = 0;
+    }
+    if (threadIdx.x == 0) sh.stash_n = 0;
+    __syncthreads();
+    for_bucket_rows(a, from_list, cand, nc, s, rows, b1,
+                    [&](uint32_t key, uint32_t) { atomicAdd(&h2[(key >> 10) & 0x7FF], 1u); });
+    __syncthreads();
+    uint32_t n_gt2;
+    const uint32_t b2 = find_bucket(h2, kHistBins, need1, sh.scan, sh.res, n_gt2);
+    const uint32_t need2 = need1 - n_gt2;
+    const uint32_t pre2 = (b1 << 11) | b2;   // key >> 10 of the level-2 bucket
+    // pass B: rows above the level-2 bucket are selected; rows inside it go
+    // to the third-digit histogram and to the LDS stash
+    for (int i = threadIdx.x; i < 1024; i += 256) sh.h3[i] = 0;
+    __syncthreads();
+    for_bucket_rows(a, from_list, cand, nc, s, rows, b1, [&](uint32_t key, uint32_t r) {
+        const uint32_t k10 = key >> 10;
+        if (k10 > pre2) {
+            atomicAdd(&sh.gtc[r / ch], 1u);
+        } else if (k10 == pre2) {
+            atomicAdd(&sh.h3[key & 0x3FF], 1u);
+            const uint32_t p = atomicAdd(&sh.stash_n, 1u);
+            if (p < (uint32_t)kStash) sh.stash[p] = ((uint64_t)key << 32) | r;
+        }
+    });
+    __syncthreads();
+    uint32_t n_gt3;
+    const uint32_t b3 = find_bucket(sh.h3, 1024, need2, sh.scan, sh.res, n_gt3);
+    const uint32_t thr = (pre2 << 10) | b3;
+    const uint32_t m_eq = need2 - n_gt3;     // rows equal to thr that are kept
+    // pass C: level-2 bucket rows above / equal to the threshold, per chunk
+    const uint32_t ns = sh.stash_n;
+    auto count_c = [&](uint32_t key, uint32_t r) {
+        if ((key >> 10) != pre2) return;
+        if (key > thr) atomicAdd(&sh.gtc[r / ch], 1u);
+        else if (key == thr) atomicAdd(&sh.eqc[r / ch], 1u);
+    };
+    if (ns <= (uint32_t)kStash) {
+        for (uint32_t i = threadIdx.x; i < ns; i += 256) count_c((uint32_t)(sh.stash[i] >> 32), (uint32_t)sh.stash[i]);
+    } else {
+        for_bucket_rows(a, from_list, cand, nc, s, rows, b1, count_c);
+    }
+    __syncthreads();
+    // ascending chunk order: equal rows go to the lowest chunks first, then
+    // output offsets are the exclusive prefix of each chunk's selected count
+    const int per = (nch + 255) / 256;
+    const int c0 = threadIdx.x * per;
+    uint32_t eq_sum = 0;
+    for (int i = c0; i < c0 + per && i < nch; i++) eq_sum += sh.eqc[i];
+    uint32_t tot;
+    uint32_t eq_before = block_excl_scan(eq_sum, sh.scan, tot);
+    uint32_t sel_sum = 0;
+    for (int i = c0; i < c0 + per && i < nch; i++) {
+        const uint32_t e = sh.eqc[i];
+        const uint32_t take = eq_before >= m_eq ? 0u : (m_eq - eq_before < e ? m_eq - eq_before : e);
+        eq_before += e;
+        sh.eqc[i] = take;
+        sel_sum += ci[i].gt + sh.gtc[i] + take;
+    }
+    uint32_t off = block_excl_scan(sel_sum, sh.scan, tot);
+    for (int i = c0; i < c0 + per && i < nch; i++) {
+        const uint32_t n_sel = ci[i].gt + sh.gtc[i] + sh.eqc[i];
+        ci[i].off = off;
+        ci[i].eq_take = sh.eqc[i];
+        off += n_sel;
+    }
+    if (threadIdx.x == 0) {
+        Threshold t;
+        t.key = thr;
+        t.mode = 1;
+        t.n_rows = (uint32_t)rows;
+        t.n_vis = (uint32_t)qi.nvis;
+        a.thr[q] = t;
+        a.cand_n[q] = 0;
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += 256) gh[i] = 0;
+}
+
+// Emit the selection in ascending token order.  grid (n_chunks, n_q), 256
+// threads; each thread takes 4 consecutive rows per 1024-row step.
+__global__ __launch_bounds__(256) void k_emit(Args a) {
+    __shared__ uint32_t scan[8];
+    const int q = blockIdx.y, c = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    if (qi.mode != 1) {
+        if (c != 0) return;
+        const int32_t cnt = qi.mode == 0 ? qi.nvis : 0;
+        for (int i = threadIdx.x; i < a.sel_ld; i += 256) dst[i] = i < cnt ? i : -1;
+        if (threadIdx.x == 0) a.sel_count[q] = cnt;
+        return;
+    }
+    const int64_t rows = qi.rows;
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    if (c >= nch) return;
+    const uint32_t thr = a.thr[q].key;
+    const ChunkInfo ci = a.chunks[(size_t)q * a.n_chunks + c];
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const int64_t r0 = (int64_t)c * a.chunk;
+    const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+    const int kp = a.kpool;
+    uint32_t eq_base = 0, out_base = ci.off;
+    for (int64_t base = r0; base < r1; base += 1024) {
+        const int64_t rb = base + 4 * threadIdx.x;
+        uint32_t key[4];
+        bool gt[4], eq[4];
+        uint32_t n_eq = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const bool ok = rb + i < r1;
+            key[i] = ok ? order_key(s[rb + i]) : 0u;
+            gt[i] = ok && key[i] > thr;
+            eq[i] = ok && key[i] == thr;
+            n_eq += eq[i];
+        }
+        uint32_t tot_eq;
+        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, scan, tot_eq);
+        bool take[4];
+        uint32_t n_take = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            take[i] = gt[i];
+            if (eq[i]) {
+                take[i] = eq_rank < ci.eq_take;
+                eq_rank++;
+            }
+            n_take += take[i];
+        }
+        uint32_t tot_take;
+        uint32_t pos = out_base + block_excl_scan(n_take, scan, tot_take);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (!take[i]) continue;
+            if (pos >= (uint32_t)a.keep) break;   // never past the kept rows
+            const int32_t r = (int32_t)(rb + i);
+            if (kp == 1) {
+                dst[pos] = r;
+            } else {
+                for (int j = 0; j < kp; j++) dst[(size_t)pos * kp + j] = r * kp + j;
+            }
+            pos++;
+        }
+        eq_base += tot_eq;
+        out_base += tot_take;
+    }
+    if (c == 0) {
+        const int32_t pooled = a.keep * kp;
+        const int32_t tail = qi.nvis - qi.rows * kp;
+        const int32_t cnt = pooled + tail;
+        for (int i = threadIdx.x; i < a.sel_ld - pooled; i += 256)
+            dst[pooled + i] = i < tail ? qi.rows * kp + i : -1;
+        if (threadIdx.x == 0) a.sel_count[q] = cnt;
+    }
+}
+
+// ---------------------------------------------------------------- attention
+// One work-group = (query q, split sp, head group hg of 16 heads); 256
+// threads = 4 waves.  The split's selected rows are processed 32 at a time,
+// staged row-major in LDS (row stride D*2 + 32 bytes) with the next step's
+// rows already in flight in registers.  Per step:
+//   QK : S^T[row][head] = C Q^T; wave (b = w & 1, kh = w >> 1) multiplies
+//        row block b (16 rows) by its half of the k-steps, the two halves
+//        are added through LDS;
+//   softmax: online, per head (one head per lane column), lazy rescale
+//        (only when the running max grows by more than 2^8); every wave
+//        keeps the same running max so that all rescale alike;
+//   PV : O^T[col][head] += V^T P^T for the wave's 128 output columns, with
+//        A = V^T read by ds_read_b64_tr_b16 and B = P split into bf16 hi + lo.
+// Work-group ids are laid out so that the four head groups of one (q, sp)
+// are dispatched to the same XCD and read the gathered rows through one L2.
+template <int D>
+struct AttnCfg {
+    static constexpr int ND = D / 32;            // MFMA k-steps of the score
+    static constexpr int NH = ND / 2;            // k-steps per half
+    static constexpr int RS = D * 2 + 32;        // LDS row stride in bytes
+    static constexpr int PPR = D / 8;            // 16-byte pieces per row
+    static constexpr int PER = kAttnRows * PPR / 256;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attend(Args a) {
+    using Cfg = AttnCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[kAttnRows * Cfg::RS];
+    __shared__ int32_t sidx[kMaxSplitRows];
+    __shared__ f32x4 sx[2][64];
+    __shared__ f32x4 pbuf[2][64];
+    __shared__ float bmax[2][16];
+
+    const int n_pairs = a.n_q * a.n_split;
+    const int within = blockIdx.x & 31;
+    const int pair = (blockIdx.x >> 5) * 8 + (within & 7);
+    const int hg = within >> 3;
+    if (pair >= n_pairs) return;
+    const int q = pair / a.n_split, sp = pair % a.n_split;
+    const QInfo qi = query_info(a, q);
+    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+    const int b = w & 1, kh = w >> 1;
+    const int head = 16 * hg + n;
+
+    int32_t count = 0;
+    if (qi.mode != 2) {
+        count = a.sel_count[q];
+        count = count < 0 ? 0 : (count > a.sel_ld ? a.sel_ld : count);
+    }
+    const int32_t start = sp * a.split_rows;
+    const int32_t nrows = (start + a.split_rows < count ? start + a.split_rows : count) - start;
+    const int32_t *selq = a.sel + (size_t)q * a.sel_ld;
+    for (int i = threadIdx.x; i < nrows; i += 256) {
+        int32_t t = selq[start + i];
+        sidx[i] = (t >= 0 && (int64_t)t < a.cache_stride) ? t : -1;
+    }
+
+    bf16x8 qreg[Cfg::NH];
+    {
+        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 32 * Cfg::NH * kh;
+#pragma unroll
+        for (int s = 0; s < Cfg::NH; s++)
+            qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * s + 8 * g));
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_part = 0.f;
+    const uint16_t *C = a.cache + (size_t)(qi.mode == 2 ? 0 : qi.seq) * a.cache_stride * D;
+    const int nch = (nrows + kAttnRows - 1) / kAttnRows;
+    __syncthreads();
+
+    u32x4 v[Cfg::PER];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < Cfg::PER; i++) {
+            const int e = threadIdx.x + 256 * i;
+            const int rr = e / Cfg::PPR, pc = e % Cfg::PPR;
+            const int r = kAttnRows * c + rr;
+            const int32_t t = r < nrows ? sidx[r] : -1;
+            v[i] = t >= 0 ? *(const u32x4 *)(C + (size_t)t * D + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if (nch > 0) fetch(0);
+
+    for (int c = 0; c < nch; c++) {
+        if (c > 0) __syncthreads();                  // previous step's PV is done with rowbuf
+#pragma unroll
+        for (int i = 0; i < Cfg::PER; i++) {
+            const int e = threadIdx.x + 256 * i;
+            const int rr = e / Cfg::PPR, pc = e % Cfg::PPR;
+            *(u32x4 *)(rowbuf + rr * Cfg::RS + 16 * pc) = v[i];
+        }
+        if (c + 1 < nch) fetch(c + 1);
+        __syncthreads();
+
+        // QK: this wave's row block and half of the k-steps
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint8_t *rp = rowbuf + (16 * b + n) * Cfg::RS + 64 * Cfg::NH * kh + 16 * g;
+#pragma unroll
+            for (int s = 0; s < Cfg::NH; s++) {
+                bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rp + 64 * s));
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[s], sa, 0, 0, 0);
+            }
+        }
+        if (kh == 1) sx[b][lane] = sa;
+        __syncthreads();
+        float z[4];
+        if (kh == 0) {
+            sa += sx[b][lane];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = kAttnRows * c + 16 * b + 4 * g + r;
+                const bool ok = row < nrows && sidx[row] >= 0;
+                z[r] = ok ? sa[r] * a.scale_log2 : -INFINITY;
+                bm = fmaxf(bm, z[r]);
+            }
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            if (g == 0) bmax[b][n] = bm;
+        }
+        __syncthreads();
+        {
+            const float cmax = fmaxf(bmax[0][n], bmax[1][n]);
+            const bool need = cmax > m_ref + 8.f;
+            if (__any(need)) {
+                const float m_new = need ? cmax : m_ref;
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+                m_ref = m_new;
+                l_part *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; i++) acc[i] *= alpha;
+            }
+        }
+        if (kh == 0) {
+            f32x4 p;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                p[r] = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+            pbuf[b][lane] = p;
+        }
+        __syncthreads();
+        bf16x8 phi, plo;
+        {
+            const f32x4 p0 = pbuf[0][lane], p1 = pbuf[1][lane];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float p = j < 4 ? p0[j] : p1[j - 4];
+                l_part += p;
+                const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
+                const float lo = p - __uint_as_float(hb);
+                phi[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+                plo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(lo) >> 16));
+            }
+        }
+        {
+            const int r_in = n >> 2, c_in = n & 3;
+            const uint8_t *v1 = rowbuf + (4 * g + r_in) * Cfg::RS + 256 * w + 8 * c_in;
+            const uint8_t *v2 = rowbuf + (16 + 4 * g + r_in) * Cfg::RS + 256 * w + 8 * c_in;
+#pragma unroll
+            for (int cb = 0; cb < 8; cb++) {
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v1 + 32 * cb));
+                const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v2 + 32 * cb));
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 tv = {t1[0], t1[1], t1[2], t1[3], t2[0], t2[1], t2[2], t2[3]};
+                const bf16x8 av = __builtin_bit_cast(bf16x8, tv);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, acc[cb], 0, 0, 0);
+            }
+        }
+    }
+    // total softmax mass per head over the four lane groups
+    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+
+    const int col0 = 128 * w + 4 * g;
+    if (a.n_split == 1) {
+        const bool bad = qi.mode == 2 || l_tot == 0.f;
+        const float inv = 1.f / l_tot;
+        float *o = a.out + ((size_t)q * kHeads + head) * kLatent + col0;
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++) {
+            f32x4 val = acc[cb] * inv;
+            if (bad) val = f32x4{NAN, NAN, NAN, NAN};
+            *(f32x4 *)(o + 16 * cb) = val;
+        }
+        if (a.lse && w == 0 && g == 0)
+            a.lse[(size_t)q * kHeads + head] = bad ? NAN : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+    } else {
+        const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + head;
+        float *o = a.pacc + slot * kLatent + col0;
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++) *(f32x4 *)(o + 16 * cb) = acc[cb];
+        if (w == 0 && g == 0) {
+            a.pml[2 * slot] = m_ref;
+            a.pml[2 * slot + 1] = l_tot;
+        }
+    }
+}
+
+// Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
+// thread four output columns.
+__global__ __launch_bounds__(128) void k_reduce(Args a) {
+    const int q = blockIdx.y, h = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    const size_t slot0 = (size_t)q * a.n_split * kHeads + h;
+    float M = -INFINITY;
+    for (int s = 0; s < a.n_split; s++) M = fmaxf(M, a.pml[2 * (slot0 + (size_t)s * kHeads)]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
+            f32x4 v[8];
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int s = s0 + i;
+                f[i] = 0.f;
+                v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (s < a.n_split) {
+                    const size_t slot = slot0 + (size_t)s * kHeads;
+                    const float m = a.pml[2 * slot];
+                    if (m != -INFINITY) {
+                        f[i] = __builtin_amdgcn_exp2f(m - M);
+                        L += a.pml[2 * slot + 1] * f[i];
+                        v[i] = *(const f32x4 *)(a.pacc + slot * kLatent + 4 * threadIdx.x);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) o += v[i] * f[i];
+        }
+    }
+    const bool bad = qi.mode == 2 || L == 0.f;
+    o = bad ? f32x4{NAN, NAN, NAN, NAN} : o * (1.f / L);
+    *(f32x4 *)(a.out + ((size_t)q * kHeads + h) * kLatent + 4 * threadIdx.x) = o;
+    if (a.lse && threadIdx.x == 0)
+        a.lse[(size_t)q * kHeads + h] = bad ? NAN : (M + __log2f(L)) * 0.69314718055994531f;
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t *)p, words);
+    return hipGetLastError();
+}
+
+hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
+    const unsigned tiles = (unsigned)((max_rows + a.score_tile - 1) / a.score_tile);
+    hipLaunchKernelGGL(k_score, dim3(tiles, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_hist(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_hist, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_filter(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_filter, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_resolve, dim3(a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_emit(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_emit, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between) {
+    // 4 head groups per (query, split); groups of 8 (query, split) pairs
+    const unsigned blocks = (unsigned)(((a.n_q * a.n_split + 7) / 8) * 32);
+    if (a.D == 576)
+        hipLaunchKernelGGL(k_attend<576>, dim3(blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_attend<512>, dim3(blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (between) between();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    hipLaunchKernelGGL(k_reduce, dim3(kHeads, a.n_q), dim3(128), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

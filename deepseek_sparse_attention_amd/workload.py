@@ -1,0 +1,45 @@
+"""Device-resident copy of a synthetic workload and one call of the fused
+step on it.  Plumbing only: torch allocates and uploads, the C ABI computes.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+from .inputs import Workload
+
+
+class DeviceWorkload:
+    """Uploads a host ``Workload`` and owns outputs and a workspace for it."""
+
+    def __init__(self, w: Workload, device: str = "cuda", sel_ld: int | None = None):
+        self.w = w
+        self.geom = w.geom
+        dev = torch.device(device)
+
+        def up(a):
+            return torch.from_numpy(a).to(dev)
+
+        self.cache = up(w.cache)
+        self.idx_k = up(w.idx_k)
+        self.q = up(w.q)
+        self.idx_q = up(w.idx_q)
+        self.idx_w = up(w.idx_w)
+        self.q_seq = up(w.q_seq)
+        self.q_nvis = up(w.q_nvis)
+        self.max_nvis = int(w.q_nvis.max())
+        self.n_q = w.n_q
+        self.sel_ld = sel_ld or (self.geom["top_k"] + self.geom["kpool"] - 1)
+        self.sel = torch.empty((self.n_q, self.sel_ld), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty(self.n_q, dtype=torch.int32, device=dev)
+        self.out = torch.empty((self.n_q, self.geom["n_heads"], self.geom["d_latent"]), dtype=torch.float32,
+                               device=dev)
+        self.lse = torch.empty((self.n_q, self.geom["n_heads"]), dtype=torch.float32, device=dev)
+        self.ws = B.new_workspace(self.geom, self.n_q, self.max_nvis, device=dev)
+        hint = self.n_q if (w.n_seq == 1 and self.n_q > 1) else 0
+        self.batch = B.batch(self.q_seq, self.q_nvis, self.max_nvis, w.n_seq, hint)
+
+    def decode_step(self, stream=None, with_sel: bool = True) -> None:
+        B.decode_step(self.geom, self.batch, self.idx_q, self.idx_w, self.idx_k, self.w.key_rows, self.q,
+                      self.cache, self.w.T, self.sel if with_sel else None, self.sel_ld,
+                      self.sel_count if with_sel else None, self.out, self.lse, self.ws, stream)

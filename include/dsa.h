@@ -1,0 +1,197 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention decode hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for a batch of queries against per-sequence caches:
+ *   1. lightning-indexer scores of every visible cached row
+ *      ("GLM 5.2 in pure C", section "The Lightning Indexer: Sparse Attention
+ *      When It Helps": a rectified dot product per indexer head, weighted and
+ *      summed across heads; TensorSharp2 GLM-5.x docs, table "The block":
+ *      32 indexer heads of width 128, top-k 2048);
+ *   2. the top-k selection that follows (same sections; ties go to the lower
+ *      index as in "GLM-5.3-Flash on WASTE", section "DeepSeek Sparse
+ *      Attention, k-pool flavour"; nothing is removed when no more than k rows
+ *      are visible, TensorSharp2 section "The sparse-attention path");
+ *   3. absorbed-MLA attention over the selected latent rows ("GLM 5.2 in pure
+ *      C", section "Attention: Multi head Latent Attention With a Tiny KV
+ *      Cache"; TensorSharp2 table "The block": 64 query heads, one 576-wide
+ *      latent row per token, softmax scale 1/16);
+ *   4. the pooled NoPE variant (WASTE "k-pool flavour"; TensorSharp2 section
+ *      "GLM-5.3-Flash (glm5next)": pools of 4 tokens, keep top_k/4 pools plus
+ *      the unpooled tail, 512-wide rows, K = V = latent).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless stated otherwise; the geometry and
+ *    batch structs are HOST structs.  bf16 tensors are raw 16-bit patterns.
+ *  - Arrays are row-major with contiguous rows; strides count rows.  Every
+ *    device base pointer must be 16-byte aligned.
+ *  - The caller owns and allocates every buffer, including the workspace
+ *    (size from dsa_workspace_bytes).  The library keeps no pointer after the
+ *    work it enqueued has finished, and allocates no device memory.
+ *  - Workspace contract: a workspace must be zero-filled once before its
+ *    first use (dsa_workspace_init, or any zero fill).  Every call restores
+ *    the counters and histograms it used to zero before its work completes,
+ *    so a workspace can be reused call after call with no clearing in
+ *    between (which keeps the hot path free of fill kernels and memsets).
+ *    After a DSA_ERR_LAUNCH, zero-fill it again.
+ *  - Work is enqueued on the caller's stream; calls return without waiting.
+ *    Calls on different streams must use different workspaces.
+ *  - Errors: every entry point validates its arguments before enqueuing
+ *    anything and returns a status.  On DSA_ERR_ARG, DSA_ERR_UNSUPPORTED,
+ *    DSA_ERR_WORKSPACE and DSA_ERR_DEVICE nothing was enqueued and no output
+ *    was written; dsa_last_error() gives a thread-local description.
+ *    DSA_ERR_LAUNCH means a kernel launch was refused: outputs are then
+ *    unspecified.  Faults after enqueue surface asynchronously, as for any
+ *    HIP call.  No entry point throws, aborts or exits.
+ *  - Per-query values that live in device memory (sequence ids, visible
+ *    counts, selection indices) cannot be checked on the host.  Kernels treat
+ *    a query whose sequence id is outside [0, n_seq) or whose visible count is
+ *    outside [1, max_nvis] as invalid: it gets sel_count 0, no selection, and
+ *    NaN output and lse.  Selection entries outside [0, cache rows) are
+ *    skipped by the attention.  No such value causes an out-of-bounds access.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dsa_bf16;
+
+enum {
+    DSA_OK = 0,
+    DSA_ERR_ARG = -1,          /* null pointer, bad size, misalignment, stride too small */
+    DSA_ERR_UNSUPPORTED = -2,  /* a geometry this library does not implement             */
+    DSA_ERR_WORKSPACE = -3,    /* workspace absent or smaller than dsa_workspace_bytes   */
+    DSA_ERR_DEVICE = -4,       /* the current HIP device is not a gfx950                 */
+    DSA_ERR_LAUNCH = -5        /* a kernel launch was refused                            */
+};
+
+/* Shape of one DSA attention layer.  Supported values: n_heads 64,
+ * d_latent 512, d_rope 64 (token-level rows of 576) or 0 (NoPE rows of 512),
+ * n_idx_heads 32, d_idx 128, kpool 1 (rows are tokens) or 4 (rows are pools),
+ * 1 <= top_k <= 4096 with top_k a multiple of kpool, softmax_scale finite
+ * and > 0 (the pages' value is 1/16).  Anything else returns
+ * DSA_ERR_UNSUPPORTED rather than being approximated. */
+typedef struct {
+    int32_t n_heads;        /* query heads (64)                                   */
+    int32_t d_latent;       /* latent width = V width = output width (512)        */
+    int32_t d_rope;         /* RoPE tail of a cache row and of a query (64 or 0)  */
+    int32_t n_idx_heads;    /* indexer heads (32)                                 */
+    int32_t d_idx;          /* indexer head width (128)                           */
+    int32_t top_k;          /* tokens kept per query (2048)                       */
+    int32_t kpool;          /* tokens per indexer row: 1, or 4 for k-pool         */
+    float softmax_scale;    /* multiplies the full (d_latent + d_rope) dot (1/16) */
+} dsa_geometry;
+
+/* The queries of one call.  A decode batch has one query per sequence with
+ * n_vis = that sequence's cached length; a chunked prefill has consecutive
+ * positions p of one sequence with n_vis = p + 1 (a query sees its own
+ * token).  "rows(q)" below is q_nvis[q] / kpool. */
+typedef struct {
+    int32_t n_q;                 /* number of queries (>= 1)                          */
+    int32_t n_seq;               /* number of sequences in the cache arrays (>= 1)    */
+    const int32_t *q_seq;        /* device [n_q] sequence of each query; NULL: query i
+                                    reads sequence i (then n_q <= n_seq)              */
+    const int32_t *q_nvis;       /* device [n_q] visible cached tokens, 1..max_nvis   */
+    int64_t max_nvis;            /* host upper bound of q_nvis, sizes grids/workspace */
+    int32_t q_per_seq_hint;      /* > 1: queries come in consecutive runs of this many
+                                    that share one sequence (prefill); runs that do
+                                    not are still handled correctly, only slower      */
+} dsa_batch;
+
+/* Bytes of workspace that dsa_topk, dsa_mla_attend and dsa_decode_step need
+ * for this geometry, query count and visible bound (the maximum of the three;
+ * one workspace serves all of them).  Returns 0 for an unsupported geometry
+ * or non-positive sizes. */
+size_t dsa_workspace_bytes(const dsa_geometry *geom, int32_t n_q, int64_t max_nvis);
+
+/* Zero-fills ws_bytes of a workspace on the stream (a fill kernel, no
+ * memset node).  DSA_OK, DSA_ERR_ARG, DSA_ERR_DEVICE or DSA_ERR_LAUNCH. */
+int dsa_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* 1. Indexer scores.
+ *   scores[q][r] = sum_h idx_w[q][h] * max(0, sum_d idx_q[q][h][d] * idx_k[seq(q)][r][d])
+ * for r < rows(q); other entries of the row are not written.
+ *   idx_q  [n_q][n_idx_heads][d_idx] bf16     idx_w [n_q][n_idx_heads] fp32
+ *   idx_k  [n_seq][key_seq_stride][d_idx] bf16 (tokens, or pool keys for kpool 4;
+ *          key_seq_stride >= max_nvis / kpool)
+ *   scores [n_q][score_ld] fp32, score_ld >= max_nvis / kpool.
+ * Accumulation is fp32 over exact bf16 products; with integer-valued inputs
+ * whose partial sums stay below 2^24 the result is exact. */
+int dsa_index_scores(const dsa_geometry *geom, const dsa_batch *batch,
+                     const dsa_bf16 *idx_q, const float *idx_w,
+                     const dsa_bf16 *idx_k, int64_t key_seq_stride,
+                     float *scores, int64_t score_ld, hipStream_t stream);
+
+/* 2. Top-k selection from scores.
+ * kpool 1: if n_vis <= top_k every visible token is selected; otherwise the
+ * first top_k tokens under (score descending, index ascending).
+ * kpool 4: if rows(q) <= top_k/4 every visible token is selected; otherwise
+ * the best top_k/4 pools under (score descending, pool ascending), expanded
+ * to their 4 tokens, followed by the unpooled tail tokens [4 rows(q), n_vis).
+ * -0.0 ranks equal to +0.0.  NaN scores are not supported.
+ *   sel [n_q][sel_ld] int32, sel_ld >= top_k + kpool - 1: token indices in
+ *   ascending order, unused slots set to -1.   sel_count [n_q] int32. */
+int dsa_topk(const dsa_geometry *geom, const dsa_batch *batch,
+             const float *scores, int64_t score_ld,
+             int32_t *sel, int32_t sel_ld, int32_t *sel_count,
+             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* 3. Absorbed-MLA attention over selected cache rows.  For each query q and
+ * head h, with D = d_latent + d_rope and t over sel[q][0..sel_count[q]):
+ *   z_t = softmax_scale * sum_{d<D} q[q][h][d] * cache[seq(q)][t][d]
+ *   out[q][h][j] = sum_t exp(z_t - m) cache[seq(q)][t][j] / sum_t exp(z_t - m),  j < d_latent
+ *   lse[q][h] = m + ln(sum_t exp(z_t - m)),  m = max_t z_t
+ *   q     [n_q][n_heads][D] bf16 (absorbed queries)
+ *   cache [n_seq][cache_seq_stride][D] bf16, cache_seq_stride >= max_nvis
+ *   out   [n_q][n_heads][d_latent] fp32;  lse [n_q][n_heads] fp32 or NULL.
+ * bf16 products, fp32 accumulation and exponentials; the result is within
+ * 2e-3 of the exact value relative to the largest |out| of the row. */
+int dsa_mla_attend(const dsa_geometry *geom, const dsa_batch *batch,
+                   const dsa_bf16 *q, const dsa_bf16 *cache, int64_t cache_seq_stride,
+                   const int32_t *sel, int32_t sel_ld, const int32_t *sel_count,
+                   float *out, float *lse,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* 4. One fused step: scores -> top-k -> attention for every query, with the
+ * scoring skipped for queries that keep every visible token.  Arguments as
+ * above; sel and sel_count may be NULL (then the selection stays in the
+ * workspace), lse may be NULL. */
+int dsa_decode_step(const dsa_geometry *geom, const dsa_batch *batch,
+                    const dsa_bf16 *idx_q, const float *idx_w,
+                    const dsa_bf16 *idx_k, int64_t key_seq_stride,
+                    const dsa_bf16 *q, const dsa_bf16 *cache, int64_t cache_seq_stride,
+                    int32_t *sel, int32_t sel_ld, int32_t *sel_count,
+                    float *out, float *lse,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Instrumentation for benchmarks.  With events set (n_events > 0), each
+ * dsa_decode_step call on this thread records events[0] on its stream before
+ * its first kernel and events[i + 1] after its i-th kernel (as many as fit),
+ * so elapsed(events[i], events[i + 1]) brackets kernel i.  Kernel order:
+ * score, filter, resolve, emit, attend, split merge (seven events in all; the merge
+ * interval is empty when the attention is not split).  Pass NULL/0 to stop.
+ * Returns DSA_OK. */
+int dsa_set_timing_events(hipEvent_t *events, int32_t n_events);
+
+/* Static description of a status code. */
+const char *dsa_status_str(int status);
+
+/* Thread-local description of the last non-OK status returned on this
+ * thread (empty string if none). */
+const char *dsa_last_error(void);
+
+/* Checks that the current HIP device is a gfx950: DSA_OK or DSA_ERR_DEVICE. */
+int dsa_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

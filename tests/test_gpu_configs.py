@@ -1,0 +1,51 @@
+"""The five problem configurations and the 128K decode point at full size,
+in the launch configuration the benchmark times (the fused step).  The
+oracle checks every query where it finishes in seconds (C0, C1, C2, C4,
+128K) and a sample of positions of the prefill chunk (C3)."""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import check_attention, check_selection, log, oracle_decode
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+from deepseek_sparse_attention_amd import inputs as I             # noqa: E402
+from deepseek_sparse_attention_amd.workload import DeviceWorkload  # noqa: E402
+
+
+def _run(name, queries=None):
+    t0 = time.time()
+    w = I.config(name)
+    log(f"{name}: generated in {time.time() - t0:.1f}s (n_q={w.n_q}, T={w.T})")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    t0 = time.time()
+    sel, cnt, out, lse = oracle_decode(w, queries)
+    log(f"{name}: oracle in {time.time() - t0:.1f}s")
+    idx = np.arange(w.n_q) if queries is None else np.asarray(queries)
+    check_selection(sel_g[idx], cnt_g[idx], sel, cnt, name)
+    check_attention(out_g[idx], lse_g[idx], out, lse, name)
+    return w, sel_g, cnt_g
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c4", "m128k"])
+def test_config_full(name):
+    _run(name)
+
+
+def test_config_c3_sampled():
+    w, sel_g, cnt_g = _run("c3", queries=[0, 1, 2, 127, 255, 256, 383, 509, 510, 511])
+    # every query keeps exactly top_k of its own visible prefix, ascending
+    for j in range(w.n_q):
+        s = sel_g[j, :cnt_g[j]]
+        assert cnt_g[j] == 2048 and np.all(np.diff(s) > 0) and s[-1] < w.q_nvis[j]

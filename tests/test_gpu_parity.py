@@ -1,0 +1,195 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, at sizes
+the oracle finishes in seconds: several score tiles, top-k chunks and
+attention splits, ragged tails, dense and sparse queries in one batch,
+token-level and k-pool geometries."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import check_attention, check_selection, log, oracle_decode, gpu_arch
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from deepseek_sparse_attention_amd import binding as B            # noqa: E402
+from deepseek_sparse_attention_amd import inputs as I             # noqa: E402
+from deepseek_sparse_attention_amd.workload import DeviceWorkload  # noqa: E402
+
+
+def setup_module():
+    arch = gpu_arch()
+    log(f"device arch {arch}")
+    assert arch.startswith("gfx950"), arch
+    B.device_check()
+
+
+def geom(kpool=1, d_rope=64, top_k=2048):
+    g = dict(I.GEOM_TOKEN)
+    g.update(kpool=kpool, d_rope=d_rope, top_k=top_k)
+    return g
+
+
+# name, geometry, n_seq, T, q_seq, q_nvis, key range
+CASES = [
+    ("tok_mixed", geom(), 2, 5003, [0, 1, 1, 0], [5003, 4097, 1500, 2049], (-8, 8)),
+    ("tok_ties", geom(), 1, 6000, [0, 0], [6000, 3001], (-1, 1)),
+    ("tok_k64", geom(top_k=64), 2, 3000, [1, 0, 1], [3000, 65, 64], (-8, 8)),
+    ("tok_k1", geom(top_k=1), 1, 1200, [0, 0], [1200, 1], (-8, 8)),
+    ("tok_k4096", geom(top_k=4096), 1, 9000, [0], [9000], (-8, 8)),
+    ("pool_mixed", geom(kpool=4, d_rope=0), 2, 12301, [0, 1, 1], [12301, 2051, 2052], (-8, 8)),
+    ("pool_k16", geom(kpool=4, d_rope=0, top_k=16), 1, 4099, [0, 0, 0], [4099, 19, 20], (-8, 8)),
+    ("pool_rope", geom(kpool=4, d_rope=64), 1, 9002, [0], [9002], (-4, 4)),
+    ("tok_nope", geom(kpool=1, d_rope=0), 1, 4500, [0], [4500], (-8, 8)),
+]
+
+
+def make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr):
+    return I.make_workload(name, 100 + i, g, n_seq, T, q_seq, q_nvis, key_range=kr)
+
+
+@pytest.mark.parametrize("case", list(enumerate(CASES)), ids=[c[0] for c in CASES])
+def test_scores_bit_exact(case):
+    i, (name, g, n_seq, T, q_seq, q_nvis, kr) = case
+    log(f"scores {name}")
+    w = make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr)
+    dw = DeviceWorkload(w)
+    rows_max = dw.max_nvis // g["kpool"]
+    ld = rows_max + 5
+    scores = torch.full((w.n_q, ld), float("nan"), device="cuda")
+    B.index_scores(g, dw.batch, dw.idx_q, dw.idx_w, dw.idx_k, w.key_rows, scores, ld)
+    torch.cuda.synchronize()
+    ref = O.index_scores(w.q_seq, w.q_nvis, g["kpool"], w.idx_q, w.idx_w, w.idx_k, score_ld=ld)
+    got = scores.cpu().numpy()
+    for j in range(w.n_q):
+        rows = int(w.q_nvis[j]) // g["kpool"]
+        assert np.array_equal(got[j, :rows], ref[j, :rows]), f"{name} q{j}"
+        assert np.isnan(got[j, rows:]).all(), f"{name} q{j} wrote past rows"
+
+
+@pytest.mark.parametrize("case", list(enumerate(CASES)), ids=[c[0] for c in CASES])
+def test_decode_step_matches_oracle(case):
+    i, (name, g, n_seq, T, q_seq, q_nvis, kr) = case
+    log(f"decode {name}")
+    w = make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr)
+    dw = DeviceWorkload(w)
+    dw.sel.fill_(-7)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, name)
+    check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, name)
+    # the histograms the call used are back to zero (workspace contract)
+    hist_bytes = w.n_q * 2048 * 4
+    assert int(dw.ws[:hist_bytes].count_nonzero()) == 0, f"{name}: histogram left dirty"
+    # a second call on the same workspace gives the same result bit for bit
+    out1, sel1 = dw.out.clone(), dw.sel.clone()
+    dw.decode_step()
+    torch.cuda.synchronize()
+    assert torch.equal(dw.sel, sel1) and torch.equal(dw.out, out1), f"{name}: second call differs"
+
+
+def _scores_case(rng, kind, n):
+    if kind == "real":
+        return rng.standard_normal(n).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(0, 5, n).astype(np.float32)
+    if kind == "zeros":
+        return np.zeros(n, np.float32)
+    if kind == "signed_zero":
+        s = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        s[rng.choice(n, min(100, n // 2), replace=False)] = 1.0
+        return s
+    if kind == "negative":
+        return -rng.integers(0, 1000, n).astype(np.float32)
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["real", "ties", "zeros", "signed_zero", "negative"])
+@pytest.mark.parametrize("kpool,top_k", [(1, 2048), (1, 7), (4, 2048), (4, 16)])
+def test_topk_bit_exact(kind, kpool, top_k):
+    """Standalone top-k on given scores, including a tie storm larger than the
+    candidate buffer (all-zero scores over 20000 rows) and -0.0 / +0.0."""
+    log(f"topk {kind} kpool={kpool} k={top_k}")
+    rng = np.random.default_rng(abs(hash((kind, kpool, top_k))) % 2**32)
+    g = geom(kpool=kpool, d_rope=0 if kpool == 4 else 64, top_k=top_k)
+    nvis = np.array([80003, 20000, top_k + kpool - 1, top_k + kpool, 5], np.int32)
+    rows = nvis // kpool
+    ld = int(rows.max())
+    s = np.stack([np.pad(_scores_case(rng, kind, int(r)), (0, ld - int(r)), constant_values=np.nan)
+                  for r in rows]).astype(np.float32)
+    sel_ref, cnt_ref = O.topk(nvis, kpool, top_k, s)
+    dev = "cuda"
+    q_nvis = torch.from_numpy(nvis).to(dev)
+    b = B.batch(None, q_nvis, int(nvis.max()), len(nvis))
+    ws = B.new_workspace(g, len(nvis), int(nvis.max()))
+    sel_ld = top_k + kpool - 1
+    sel = torch.full((len(nvis), sel_ld), -9, dtype=torch.int32, device=dev)
+    cnt = torch.full((len(nvis),), -9, dtype=torch.int32, device=dev)
+    st = torch.from_numpy(s).to(dev)
+    B.topk(g, b, st, ld, sel, sel_ld, cnt, ws)
+    torch.cuda.synchronize()
+    check_selection(sel.cpu().numpy(), cnt.cpu().numpy(), sel_ref, cnt_ref, f"{kind}/{kpool}/{top_k}")
+    # twice in a row on the same workspace
+    B.topk(g, b, st, ld, sel, sel_ld, cnt, ws)
+    torch.cuda.synchronize()
+    check_selection(sel.cpu().numpy(), cnt.cpu().numpy(), sel_ref, cnt_ref, f"{kind}/{kpool}/{top_k} again")
+
+
+@pytest.mark.parametrize("d_rope", [64, 0])
+@pytest.mark.parametrize("count", [1, 31, 32, 33, 100, 2048, 2051])
+def test_attend_matches_oracle(d_rope, count):
+    log(f"attend d_rope={d_rope} count={count}")
+    rng = np.random.default_rng(count * 7 + d_rope)
+    g = geom(kpool=4 if d_rope == 0 else 1, d_rope=d_rope)
+    D = 512 + d_rope
+    T = 6000
+    cache = I.f32_to_bf16_bits(rng.standard_normal((2, T, D)).astype(np.float32))
+    n_q = 3
+    q = I.f32_to_bf16_bits(rng.standard_normal((n_q, 64, D)).astype(np.float32))
+    q_seq = np.array([0, 1, 1], np.int32)
+    sel_ld = g["top_k"] + g["kpool"] - 1
+    sel = np.full((n_q, sel_ld), -1, np.int32)
+    cnt = np.zeros(n_q, np.int32)
+    for j in range(n_q):
+        c = min(count, sel_ld)
+        sel[j, :c] = np.sort(rng.choice(T, c, replace=False))
+        cnt[j] = c
+    out_ref, lse_ref = O.mla_attend(q_seq, 512, d_rope, 1 / 16, q, cache, sel, cnt)
+    dev = "cuda"
+    b = B.batch(torch.from_numpy(q_seq).to(dev), torch.full((n_q,), T, dtype=torch.int32, device=dev), T, 2)
+    ws = B.new_workspace(g, n_q, T)
+    out = torch.full((n_q, 64, 512), float("nan"), device=dev)
+    lse = torch.full((n_q, 64), float("nan"), device=dev)
+    B.mla_attend(g, b, torch.from_numpy(q).to(dev), torch.from_numpy(cache).to(dev), T,
+                 torch.from_numpy(sel).to(dev), sel_ld, torch.from_numpy(cnt).to(dev), out, lse, ws)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), out_ref, lse_ref, f"attend D={D} n={count}")
+
+
+def test_prefill_chunk_small():
+    """Chunked prefill at positions 0..511 of a 4096-token context: early
+    queries keep all their candidates, later ones select."""
+    log("prefill c3s")
+    w = I.c3_small()
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, "c3s")
+    check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, "c3s")
+
+
+def test_prefill_chunk_sparse_small():
+    """Prefill chunk past the budget: 300 positions at the end of 6000."""
+    log("prefill tail chunk")
+    T = 6000
+    pos = np.arange(T - 300, T)
+    w = I.make_workload("pf", 14, I.GEOM_TOKEN, 1, T, np.zeros(300), pos + 1)
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, "prefill tail")
+    check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, "prefill tail")
