@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "DSA decode queries/sec at 128K ctx, top-k 2048; achieved HBM GB/s vs peak"
-KERNELS = ["score", "filter", "resolve", "emit", "attend", "merge"]
+KERNELS = ["score", "filter", "emit", "attend", "merge"]
 
 
 def algorithmic_bytes(w):
@@ -75,6 +75,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=6.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (to scale byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -159,6 +161,13 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": score_bytes},
     }
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = src.numel()
     if not args.no_cpu_baseline:
         del reps
         torch.cuda.empty_cache()

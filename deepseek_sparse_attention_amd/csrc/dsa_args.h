@@ -30,14 +30,14 @@ struct Args {
     int32_t *sel_count;
     float *out, *lse;
     // workspace
-    uint32_t *hist, *cand_n, *done;
-    Threshold *thr;
+    uint32_t *hist;
     ChunkInfo *chunks;
     uint64_t *cand;
     float *pacc, *pml;
     // plan
     int32_t chunk, n_chunks, cand_cap, split_rows, n_split, score_tile;
     int32_t fused;        // 1: dense queries are not scored, histogram accumulated
+    int32_t clear_topk;   // 1: attention zeroes the top-k histogram
 };
 
 }  // namespace dsa

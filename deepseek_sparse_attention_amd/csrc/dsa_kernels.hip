@@ -138,14 +138,21 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
 }
 
 // ---------------------------------------------------------------- scores
-// grid (tiles, n_q), 256 threads.  Wave w of a work-group takes 64-row steps
-// t0 + 64 (w + 4 i).  Per 16 rows: A = idx_q (heads x d, two 16-head blocks,
-// from registers), B = keys^T (d x rows) loaded straight from memory in the
-// MFMA operand layout: lane (g = l/16, n = l%16) holds row n, d in
-// [32 s + 8 g, +8) for k-step s.  D[head][row] lands as lane (g, n) holding
-// heads 4g + r (+16) of row n.
+// grid (tiles, n_q), 256 threads.  Wave w of a work-group takes 64-row
+// steps t0 + 64 (w + 4 i).  Keys are read with fully coalesced 16-byte loads
+// (one wave instruction = 1 KiB = 4 rows), the next step's 16 KiB already in
+// flight in registers while the current one is computed; each step is staged
+// in the wave's own LDS tile with the 16-byte pieces of row r stored at
+// slot (piece ^ (r & 7)), so that both the row-major store and the MFMA
+// operand reads below are free of bank conflicts.  Per 16 rows:
+// A = idx_q (heads x d, two 16-head blocks, from registers), B = keys^T
+// (d x rows): lane (g = l/16, n = l%16) takes row n, d in [32 s + 8 g, +8)
+// for k-step s.  D[head][row] lands as lane (g, n) holding heads 4g + r
+// (+16) of row n; the epilogue applies ReLU and the head weights and sums
+// the four lane groups.
 __global__ __launch_bounds__(256) void k_score(Args a) {
     __shared__ uint32_t lhist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[4][64 * 256];
     const int q = blockIdx.y;
     const QInfo qi = query_info(a, q);
     if (qi.mode == 2) return;
@@ -173,38 +180,51 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)q * kIdxHeads + 16 * mb + 4 * g + r];
     }
-    const uint16_t *K = a.idx_k + (size_t)qi.seq * a.key_stride * kIdxDim;
+    const uint8_t *K = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)qi.seq * a.key_stride * kIdxDim);
     float *srow = a.scores + (size_t)q * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
+    uint8_t *tb = tiles[w];
+    const int64_t end = t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
 
-    for (int64_t base = t0 + 64 * w; base < t0 + a.score_tile && base < rows; base += 256) {
-        u32x4 v[4][4];
+    u32x4 v[16];
+    auto fetch = [&](int64_t base) {
 #pragma unroll
-        for (int st = 0; st < 4; st++) {
-            int64_t r = base + 16 * st + n;
+        for (int i = 0; i < 16; i++) {
+            int64_t r = base + 4 * i + (lane >> 4);
             r = r < rows ? r : rows - 1;
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-                v[st][s] = __builtin_nontemporal_load((const u32x4 *)(K + r * kIdxDim + 32 * s + 8 * g));
+            v[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (lane & 15)));
         }
+    };
+    int64_t base = t0 + 64 * w;
+    if (base < end) fetch(base);
+    for (; base < end; base += 256) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int r = 4 * i + (lane >> 4), pc = lane & 15;
+            *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 7))) = v[i];
+        }
+        if (base + 256 < end) fetch(base + 256);
+        __builtin_amdgcn_wave_barrier();
         float p[4];
 #pragma unroll
         for (int st = 0; st < 4; st++) {
+            const int r = 16 * st + n;
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                bf16x8 b = __builtin_bit_cast(bf16x8, v[st][s]);
+                const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], b, acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], b, acc1, 0, 0, 0);
             }
             float x = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                x += wt[0][r] * fmaxf(acc0[r], 0.f);
-                x += wt[1][r] * fmaxf(acc1[r], 0.f);
+            for (int rr = 0; rr < 4; rr++) {
+                x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
+                x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
             }
             p[st] = x;
         }
+        __builtin_amdgcn_wave_barrier();
         // sum the four lane groups; each lane keeps one of the four 16-row steps
         const bool b0 = g & 1, b1 = (g >> 1) & 1;
         const float send0 = b0 ? p[0] : p[2], send1 = b0 ? p[1] : p[3];
@@ -213,9 +233,9 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
         const float q1 = keep1 + __shfl_xor(send1, 16, 64);
         const float score = (b1 ? q1 : q0) + __shfl_xor(b1 ? q0 : q1, 32, 64);
         const int64_t row = base + 16 * st_mine + n;
-        if (row < rows) {
+        if (row < end) {
             srow[row] = score;
-            if (hist) atomicAdd(&lhist[order_key(score) >> 21], 1u);
+            if (hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
         }
     }
     if (hist) {
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
     for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
     __syncthreads();
     const float *s = a.scores_in + (size_t)q * a.score_ld;
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) atomicAdd(&lhist[order_key(s[r]) >> 21], 1u);
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) atomicAdd(&lhist[order_key(s[r]) >> 20], 1u);
     __syncthreads();
     uint32_t *gh = a.hist + (size_t)q * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += 256)
@@ -247,59 +267,30 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
 }
 
 // ---------------------------------------------------------------- top-k
-// Pass over each chunk: count rows above the threshold bucket, collect the
-// bucket's rows as candidates.  The last chunk of a query to finish resolves
-// the exact threshold and the per-chunk output offsets, then restores the
-// query's histogram and counters to zero.  grid (n_chunks, n_q), 256 threads.
-constexpr int kStash = 4096;     // rows of the level-2 bucket kept in LDS
+// Exact radix select over 32-bit order keys, ranked by (key descending,
+// row ascending), three digits: bits 31..20 (4096-bin histogram from the
+// score kernel or k_hist), bits 19..10 and bits 9..0.
+//   k_filter (grid chunks x queries): from the first-digit histogram find the
+//     bucket b1 holding the keep-th row; count the chunk's rows above b1 and
+//     copy the bucket's rows (key, row) into the chunk's own candidate slots.
+//   k_emit (same grid): every work-group gathers all candidates of its query
+//     into LDS, resolves the exact threshold from them (second and third
+//     digit), derives its chunk's output offset and its share of the rows
+//     equal to the threshold (lowest chunks first), then writes its
+//     selected rows in ascending order.
+// No global atomics: chunks own their candidate slots; if a chunk's bucket
+// rows overflow them, or all candidates overflow the LDS copy, k_emit
+// derives the candidates from the scores instead (slow, exact).
 
-struct ResolveShared {
-    uint32_t hist[kHistBins];     // first digit, then reused for the second
-    uint32_t h3[1024];            // third digit
-    uint32_t gtc[kMaxChunks];     // per chunk: bucket rows above the threshold
-    uint32_t eqc[kMaxChunks];     // per chunk: rows equal to the threshold
-    uint64_t stash[kStash];       // (key, row) of the level-2 bucket
-    uint32_t scan[8];
-    uint32_t res[4];
-    uint32_t stash_n;
-};
-
-// Candidates (order key, row) of the first-digit bucket, read in rounds of
-// 16 per thread so that each round costs one memory round trip.  From the
-// candidate list when it fits, else by re-deriving them from the scores.
-template <class F>
-__device__ __forceinline__ void for_bucket_rows(const Args &a, bool from_list, const uint64_t *cand, uint32_t nc,
-                                                const float *s, int64_t rows, uint32_t b1, F &&f) {
-    if (from_list) {
-        for (uint32_t base = 0; base < nc; base += 16 * 256) {
-            uint64_t e[16];
+__device__ __forceinline__ void load_hist(const uint32_t *gh, uint32_t *lh) {
+    uint32_t v[kHistBins / 256];
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const uint32_t i = base + 256 * j + threadIdx.x;
-                e[j] = i < nc ? cand[i] : 0ull;
-            }
+    for (int i = 0; i < kHistBins / 256; i++) v[i] = gh[threadIdx.x + 256 * i];
 #pragma unroll
-            for (int j = 0; j < 16; j++)
-                if (e[j]) f((uint32_t)(e[j] >> 32), (uint32_t)e[j]);
-        }
-    } else {
-        for (int64_t base = 0; base < rows; base += 16 * 256) {
-            float v[16];
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const int64_t r = base + 256 * j + threadIdx.x;
-                v[j] = r < rows ? s[r] : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const int64_t r = base + 256 * j + threadIdx.x;
-                const uint32_t key = order_key(v[j]);
-                if (r < rows && (key >> 21) == b1) f(key, (uint32_t)r);
-            }
-        }
-    }
+    for (int i = 0; i < kHistBins / 256; i++) lh[threadIdx.x + 256 * i] = v[i];
 }
 
+// grid (n_chunks, n_q), 256 threads.
 __global__ __launch_bounds__(256) void k_filter(Args a) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t scan[8];
@@ -310,170 +301,79 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     const int64_t rows = qi.rows;
     const int nch = (int)((rows + a.chunk - 1) / a.chunk);
     if (c >= nch) return;
-    const uint32_t keep = (uint32_t)a.keep;
-    uint32_t *gh = a.hist + (size_t)q * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) hist[i] = gh[i];
-    __syncthreads();
-    uint32_t n_gt1;
-    const uint32_t b1 = find_bucket(hist, kHistBins, keep, scan, res, n_gt1);
-
     const float *s = a.scores_in + (size_t)q * a.score_ld;
     const int64_t r0 = (int64_t)c * a.chunk;
     const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
-    uint64_t *cand = a.cand + (size_t)q * a.cand_cap;
-    uint32_t gt = 0;
-    // blocks of 2048 rows, 8 per thread; one atomic per block reserves the
-    // block's candidate slots (same-address atomics from every work-group
-    // would serialize)
+    // first block of scores in flight while the threshold bucket is found
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int64_t r = r0 + 256 * i + threadIdx.x;
+        sv[i] = r < r1 ? s[r] : 0.f;
+    }
+    load_hist(a.hist + (size_t)q * kHistBins, hist);
+    __syncthreads();
+    uint32_t n_gt1;
+    const uint32_t b1 = find_bucket(hist, kHistBins, (uint32_t)a.keep, scan, res, n_gt1);
+
+    uint64_t *slots = a.cand + ((size_t)q * a.n_chunks + c) * a.cand_cap;
+    uint32_t gt = 0, n_cand = 0;
     for (int64_t sb = r0; sb < r1; sb += 2048) {
+        if (sb != r0) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int64_t r = sb + 256 * i + threadIdx.x;
+                sv[i] = r < r1 ? s[r] : 0.f;
+            }
+        }
         uint32_t keys[8];
         uint32_t n_c = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int64_t r = sb + 256 * i + threadIdx.x;
-            uint32_t key = 0;
-            bool is_c = false;
-            if (r < r1) {
-                key = order_key(s[r]);
-                const uint32_t d1 = key >> 21;
-                gt += d1 > b1 ? 1u : 0u;
-                is_c = d1 == b1;
-            }
+            const uint32_t key = order_key(sv[i]);
+            const bool ok = r < r1;
+            const uint32_t d1 = key >> 20;
+            gt += (ok && d1 > b1) ? 1u : 0u;
+            const bool is_c = ok && d1 == b1;
             keys[i] = is_c ? key : 0u;
             n_c += is_c ? 1u : 0u;
         }
         uint32_t tot;
-        const uint32_t excl = block_excl_scan(n_c, scan, tot);
-        if (tot == 0) continue;
-        if (threadIdx.x == 0) res[2] = atomicAdd(&a.cand_n[q], tot);
-        __syncthreads();
-        uint32_t pos = res[2] + excl;
-        __syncthreads();
+        uint32_t pos = n_cand + block_excl_scan(n_c, scan, tot);
+        n_cand += tot;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             if (!keys[i]) continue;      // order keys of real scores are never 0
             const int64_t r = sb + 256 * i + threadIdx.x;
-            if (pos < (uint32_t)a.cand_cap) cand[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)r;
+            if (pos < (uint32_t)a.cand_cap) slots[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)r;
             pos++;
         }
     }
     gt = block_sum(gt, scan);
-    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
-    if (threadIdx.x == 0) ci[c].gt = gt;
-}
-
-// Exact threshold of each sparse query from its first-digit histogram and
-// the collected candidates: two more radix digits, then each chunk's output
-// offset and its share of the rows equal to the threshold (lowest chunks
-// first).  Restores the query's histogram and counter to zero.  grid (n_q),
-// 256 threads.
-__global__ __launch_bounds__(256) void k_resolve(Args a) {
-    __shared__ ResolveShared sh;
-    const int q = blockIdx.x;
-    const QInfo qi = query_info(a, q);
-    if (qi.mode != 1) return;
-    const int64_t rows = qi.rows;
-    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-    const uint32_t keep = (uint32_t)a.keep;
-    uint32_t *gh = a.hist + (size_t)q * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) sh.hist[i] = gh[i];
-    __syncthreads();
-    uint32_t n_gt1;
-    const uint32_t b1 = find_bucket(sh.hist, kHistBins, keep, sh.scan, sh.res, n_gt1);
-    const float *s = a.scores_in + (size_t)q * a.score_ld;
-    const uint64_t *cand = a.cand + (size_t)q * a.cand_cap;
-    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
-    const uint32_t nc = a.cand_n[q];
-    const bool from_list = nc <= (uint32_t)a.cand_cap;
-    const uint32_t need1 = keep - n_gt1;
-    const uint32_t ch = (uint32_t)a.chunk;
-    // pass A: second digit (key bits 20..10) over the bucket
-    uint32_t *h2 = sh.hist;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) h2[i] = 0;
-    for (int i = threadIdx.x; i < nch; i += 256) {
-        sh.gtc[i] = 0;
-        sh.eqc[i] = 0;
-    }
-    if (threadIdx.x == 0) sh.stash_n = 0;
-    __syncthreads();
-    for_bucket_rows(a, from_list, cand, nc, s, rows, b1,
-                    [&](uint32_t key, uint32_t) { atomicAdd(&h2[(key >> 10) & 0x7FF], 1u); });
-    __syncthreads();
-    uint32_t n_gt2;
-    const uint32_t b2 = find_bucket(h2, kHistBins, need1, sh.scan, sh.res, n_gt2);
-    const uint32_t need2 = need1 - n_gt2;
-    const uint32_t pre2 = (b1 << 11) | b2;   // key >> 10 of the level-2 bucket
-    // pass B: rows above the level-2 bucket are selected; rows inside it go
-    // to the third-digit histogram and to the LDS stash
-    for (int i = threadIdx.x; i < 1024; i += 256) sh.h3[i] = 0;
-    __syncthreads();
-    for_bucket_rows(a, from_list, cand, nc, s, rows, b1, [&](uint32_t key, uint32_t r) {
-        const uint32_t k10 = key >> 10;
-        if (k10 > pre2) {
-            atomicAdd(&sh.gtc[r / ch], 1u);
-        } else if (k10 == pre2) {
-            atomicAdd(&sh.h3[key & 0x3FF], 1u);
-            const uint32_t p = atomicAdd(&sh.stash_n, 1u);
-            if (p < (uint32_t)kStash) sh.stash[p] = ((uint64_t)key << 32) | r;
-        }
-    });
-    __syncthreads();
-    uint32_t n_gt3;
-    const uint32_t b3 = find_bucket(sh.h3, 1024, need2, sh.scan, sh.res, n_gt3);
-    const uint32_t thr = (pre2 << 10) | b3;
-    const uint32_t m_eq = need2 - n_gt3;     // rows equal to thr that are kept
-    // pass C: level-2 bucket rows above / equal to the threshold, per chunk
-    const uint32_t ns = sh.stash_n;
-    auto count_c = [&](uint32_t key, uint32_t r) {
-        if ((key >> 10) != pre2) return;
-        if (key > thr) atomicAdd(&sh.gtc[r / ch], 1u);
-        else if (key == thr) atomicAdd(&sh.eqc[r / ch], 1u);
-    };
-    if (ns <= (uint32_t)kStash) {
-        for (uint32_t i = threadIdx.x; i < ns; i += 256) count_c((uint32_t)(sh.stash[i] >> 32), (uint32_t)sh.stash[i]);
-    } else {
-        for_bucket_rows(a, from_list, cand, nc, s, rows, b1, count_c);
-    }
-    __syncthreads();
-    // ascending chunk order: equal rows go to the lowest chunks first, then
-    // output offsets are the exclusive prefix of each chunk's selected count
-    const int per = (nch + 255) / 256;
-    const int c0 = threadIdx.x * per;
-    uint32_t eq_sum = 0;
-    for (int i = c0; i < c0 + per && i < nch; i++) eq_sum += sh.eqc[i];
-    uint32_t tot;
-    uint32_t eq_before = block_excl_scan(eq_sum, sh.scan, tot);
-    uint32_t sel_sum = 0;
-    for (int i = c0; i < c0 + per && i < nch; i++) {
-        const uint32_t e = sh.eqc[i];
-        const uint32_t take = eq_before >= m_eq ? 0u : (m_eq - eq_before < e ? m_eq - eq_before : e);
-        eq_before += e;
-        sh.eqc[i] = take;
-        sel_sum += ci[i].gt + sh.gtc[i] + take;
-    }
-    uint32_t off = block_excl_scan(sel_sum, sh.scan, tot);
-    for (int i = c0; i < c0 + per && i < nch; i++) {
-        const uint32_t n_sel = ci[i].gt + sh.gtc[i] + sh.eqc[i];
-        ci[i].off = off;
-        ci[i].eq_take = sh.eqc[i];
-        off += n_sel;
-    }
     if (threadIdx.x == 0) {
-        Threshold t;
-        t.key = thr;
-        t.mode = 1;
-        t.n_rows = (uint32_t)rows;
-        t.n_vis = (uint32_t)qi.nvis;
-        a.thr[q] = t;
-        a.cand_n[q] = 0;
+        ChunkInfo info;
+        info.gt = gt;
+        info.n_cand = n_cand;
+        a.chunks[(size_t)q * a.n_chunks + c] = info;
     }
-    for (int i = threadIdx.x; i < kHistBins; i += 256) gh[i] = 0;
 }
 
-// Emit the selection in ascending token order.  grid (n_chunks, n_q), 256
-// threads; each thread takes 4 consecutive rows per 1024-row step.
+constexpr int kLdsCand = 6144;   // candidates k_emit keeps in LDS
+
+struct EmitShared {
+    uint32_t h[kHistBins];        // first digit, then the second (1024 bins)
+    uint32_t h3[1024];            // third digit
+    uint32_t pre[kMaxChunks + 1]; // exclusive prefix of the chunks' candidate counts
+    uint64_t cand[kLdsCand];
+    uint32_t scan[8];
+    uint32_t res[4];
+};
+
+// grid (n_chunks, n_q), 256 threads; each thread takes 4 consecutive rows
+// per 1024-row step of its chunk.
 __global__ __launch_bounds__(256) void k_emit(Args a) {
-    __shared__ uint32_t scan[8];
+    __shared__ EmitShared sh;
     const int q = blockIdx.y, c = blockIdx.x;
     const QInfo qi = query_info(a, q);
     int32_t *dst = a.sel + (size_t)q * a.sel_ld;
@@ -487,13 +387,127 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
     const int64_t rows = qi.rows;
     const int nch = (int)((rows + a.chunk - 1) / a.chunk);
     if (c >= nch) return;
-    const uint32_t thr = a.thr[q].key;
-    const ChunkInfo ci = a.chunks[(size_t)q * a.n_chunks + c];
+    const uint32_t keep = (uint32_t)a.keep;
     const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
+    const uint64_t *slots = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
+    const uint32_t ch = (uint32_t)a.chunk;
+
+    // per-chunk counts: rows above the first-digit bucket before this chunk,
+    // and the candidate layout (each chunk's slots are packed in LDS)
+    uint32_t gt1_before = 0, my_nc = 0;
+    bool overflow = false;
+    const int per = (nch + 255) / 256;
+    const int c0 = threadIdx.x * per;
+    for (int i = c0; i < c0 + per && i < nch; i++) {
+        const ChunkInfo info = ci[i];
+        if (i < c) gt1_before += info.gt;
+        overflow |= info.n_cand > (uint32_t)a.cand_cap;
+        my_nc += info.n_cand < (uint32_t)a.cand_cap ? info.n_cand : (uint32_t)a.cand_cap;
+    }
+    load_hist(a.hist + (size_t)q * kHistBins, sh.h);
+    uint32_t n_all;
+    uint32_t run = block_excl_scan(my_nc, sh.scan, n_all);
+    for (int i = c0; i < c0 + per && i < nch; i++) {
+        sh.pre[i] = run;
+        const uint32_t n = ci[i].n_cand;
+        run += n < (uint32_t)a.cand_cap ? n : (uint32_t)a.cand_cap;
+    }
+    if (threadIdx.x == 0) sh.pre[nch] = n_all;
+    overflow = __syncthreads_or(overflow) || n_all > (uint32_t)kLdsCand;
+    uint32_t n_gt1;
+    const uint32_t b1 = find_bucket(sh.h, kHistBins, keep, sh.scan, sh.res, n_gt1);
+    const uint32_t need1 = keep - n_gt1;
+
+    // all candidates into LDS (rounds of 16 per thread), second digit
+    uint32_t *h2 = sh.h;
+    __syncthreads();
+    for (int i = threadIdx.x; i < 1024; i += 256) {
+        h2[i] = 0;
+        sh.h3[i] = 0;
+    }
+    __syncthreads();
+    if (!overflow) {
+        for (uint32_t base = 0; base < n_all; base += 16 * 256) {
+            uint64_t e[16];
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const uint32_t i = base + 256 * j + threadIdx.x;
+                e[j] = 0;
+                if (i < n_all) {
+                    int lo = 0, hi = nch;          // chunk k with pre[k] <= i < pre[k+1]
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (sh.pre[mid] <= i) lo = mid;
+                        else hi = mid;
+                    }
+                    e[j] = slots[(size_t)lo * a.cand_cap + (i - sh.pre[lo])];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const uint32_t i = base + 256 * j + threadIdx.x;
+                if (i < n_all) {
+                    sh.cand[i] = e[j];
+                    atomicAdd(&h2[(uint32_t)(e[j] >> 42) & 0x3FF], 1u);
+                }
+            }
+        }
+    } else {
+        for (int64_t r = threadIdx.x; r < rows; r += 256) {
+            const uint32_t key = order_key(s[r]);
+            if ((key >> 20) == b1) atomicAdd(&h2[(key >> 10) & 0x3FF], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t n_gt2;
+    const uint32_t b2 = find_bucket(h2, 1024, need1, sh.scan, sh.res, n_gt2);
+    const uint32_t need2 = need1 - n_gt2;
+    const uint32_t pre2 = (b1 << 10) | b2;   // key >> 10 of the level-2 bucket
+    // third digit within the level-2 bucket; bucket rows of earlier chunks
+    // above the level-2 bucket are selected
+    uint32_t gt2_before = 0;
+    auto pass3 = [&](uint32_t key, uint32_t r) {
+        const uint32_t k10 = key >> 10;
+        if (k10 > pre2) gt2_before += (r / ch < (uint32_t)c) ? 1u : 0u;
+        else if (k10 == pre2) atomicAdd(&sh.h3[key & 0x3FF], 1u);
+    };
+    if (!overflow) {
+        for (uint32_t i = threadIdx.x; i < n_all; i += 256) pass3((uint32_t)(sh.cand[i] >> 32), (uint32_t)sh.cand[i]);
+    } else {
+        for (int64_t r = threadIdx.x; r < rows; r += 256) {
+            const uint32_t key = order_key(s[r]);
+            if ((key >> 20) == b1) pass3(key, (uint32_t)r);
+        }
+    }
+    __syncthreads();
+    uint32_t n_gt3;
+    const uint32_t b3 = find_bucket(sh.h3, 1024, need2, sh.scan, sh.res, n_gt3);
+    const uint32_t thr = (pre2 << 10) | b3;
+    const uint32_t m_eq = need2 - n_gt3;     // rows equal to thr that are kept
+    uint32_t gt3_before = 0, eq_before = 0;
+    auto pass4 = [&](uint32_t key, uint32_t r) {
+        if ((key >> 10) != pre2 || r / ch >= (uint32_t)c) return;
+        gt3_before += key > thr ? 1u : 0u;
+        eq_before += key == thr ? 1u : 0u;
+    };
+    if (!overflow) {
+        for (uint32_t i = threadIdx.x; i < n_all; i += 256) pass4((uint32_t)(sh.cand[i] >> 32), (uint32_t)sh.cand[i]);
+    } else {
+        for (int64_t r = threadIdx.x; r < rows; r += 256) {
+            const uint32_t key = order_key(s[r]);
+            if ((key >> 20) == b1) pass4(key, (uint32_t)r);
+        }
+    }
+    const uint32_t before_gt = block_sum(gt1_before + gt2_before + gt3_before, sh.scan);
+    const uint32_t eq_b = block_sum(eq_before, sh.scan);
+    const uint32_t eq_taken = eq_b < m_eq ? eq_b : m_eq;
+    const uint32_t eq_take = m_eq - eq_taken;       // this chunk keeps its first eq_take equal rows
+
     const int64_t r0 = (int64_t)c * a.chunk;
     const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
     const int kp = a.kpool;
-    uint32_t eq_base = 0, out_base = ci.off;
+    uint32_t eq_base = 0, out_base = before_gt + eq_taken;
     for (int64_t base = r0; base < r1; base += 1024) {
         const int64_t rb = base + 4 * threadIdx.x;
         uint32_t key[4];
@@ -508,24 +522,24 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
             n_eq += eq[i];
         }
         uint32_t tot_eq;
-        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, scan, tot_eq);
+        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, sh.scan, tot_eq);
         bool take[4];
         uint32_t n_take = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             take[i] = gt[i];
             if (eq[i]) {
-                take[i] = eq_rank < ci.eq_take;
+                take[i] = eq_rank < eq_take;
                 eq_rank++;
             }
             n_take += take[i];
         }
         uint32_t tot_take;
-        uint32_t pos = out_base + block_excl_scan(n_take, scan, tot_take);
+        uint32_t pos = out_base + block_excl_scan(n_take, sh.scan, tot_take);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             if (!take[i]) continue;
-            if (pos >= (uint32_t)a.keep) break;   // never past the kept rows
+            if (pos >= keep) break;                 // never past the kept rows
             const int32_t r = (int32_t)(rb + i);
             if (kp == 1) {
                 dst[pos] = r;
@@ -546,6 +560,14 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
         if (threadIdx.x == 0) a.sel_count[q] = cnt;
     }
 }
+
+// Zeroes a query's first-digit histogram (after a standalone
+// top-k; the fused step does this in the attention kernel).  grid (n_q).
+__device__ __forceinline__ void clear_topk_state(const Args &a, int q) {
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) a.hist[(size_t)q * kHistBins + i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_topk_clear(Args a) { clear_topk_state(a, blockIdx.x); }
 
 // ---------------------------------------------------------------- attention
 // One work-group = (query q, split sp, head group hg of 16 heads); 256
@@ -586,6 +608,7 @@ __global__ __launch_bounds__(256) void k_attend(Args a) {
     const int hg = within >> 3;
     if (pair >= n_pairs) return;
     const int q = pair / a.n_split, sp = pair % a.n_split;
+    if (a.clear_topk && sp == 0 && hg == 0) clear_topk_state(a, q);
     const QInfo qi = query_info(a, q);
     const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
     const int b = w & 1, kh = w >> 1;
@@ -750,37 +773,44 @@ __global__ __launch_bounds__(256) void k_attend(Args a) {
 }
 
 // Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
-// thread four output columns.
+// thread four output columns.  Up to 16 splits are loaded in one round trip
+// and merged online (running max, rescaled sums).
 __global__ __launch_bounds__(128) void k_reduce(Args a) {
+    constexpr int MB = 16;
     const int q = blockIdx.y, h = blockIdx.x;
     const QInfo qi = query_info(a, q);
     const size_t slot0 = (size_t)q * a.n_split * kHeads + h;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; s++) M = fmaxf(M, a.pml[2 * (slot0 + (size_t)s * kHeads)]);
-    float L = 0.f;
+    float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
-            f32x4 v[8];
-            float f[8];
+    for (int s0 = 0; s0 < a.n_split; s0 += MB) {
+        f32x4 v[MB];
+        float m[MB], l[MB];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int s = s0 + i;
-                f[i] = 0.f;
-                v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (s < a.n_split) {
-                    const size_t slot = slot0 + (size_t)s * kHeads;
-                    const float m = a.pml[2 * slot];
-                    if (m != -INFINITY) {
-                        f[i] = __builtin_amdgcn_exp2f(m - M);
-                        L += a.pml[2 * slot + 1] * f[i];
-                        v[i] = *(const f32x4 *)(a.pacc + slot * kLatent + 4 * threadIdx.x);
-                    }
-                }
+        for (int i = 0; i < MB; i++) {
+            m[i] = -INFINITY;
+            l[i] = 0.f;
+            v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s0 + i < a.n_split) {
+                const size_t slot = slot0 + (size_t)(s0 + i) * kHeads;
+                m[i] = a.pml[2 * slot];
+                l[i] = a.pml[2 * slot + 1];
+                v[i] = *(const f32x4 *)(a.pacc + slot * kLatent + 4 * threadIdx.x);
             }
-#pragma unroll
-            for (int i = 0; i < 8; i++) o += v[i] * f[i];
         }
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < MB; i++) Mn = fmaxf(Mn, m[i]);
+        if (Mn == -INFINITY) continue;
+        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        L *= fo;
+        o *= fo;
+#pragma unroll
+        for (int i = 0; i < MB; i++) {
+            const float f = m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - Mn);
+            L += l[i] * f;
+            o += v[i] * f;
+        }
+        M = Mn;
     }
     const bool bad = qi.mode == 2 || L == 0.f;
     o = bad ? f32x4{NAN, NAN, NAN, NAN} : o * (1.f / L);
@@ -815,8 +845,8 @@ hipError_t launch_filter(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_resolve(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_resolve, dim3(a.n_q), dim3(256), 0, st, a);
+hipError_t launch_topk_clear(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk_clear, dim3(a.n_q), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -12,10 +12,9 @@ constexpr int kHeads = 64;        // query heads
 constexpr int kLatent = 512;      // latent / V / output width
 constexpr int kIdxHeads = 32;     // indexer heads
 constexpr int kIdxDim = 128;      // indexer head width
-constexpr int kHistBins = 2048;   // first radix digit: order-key bits 31..21
+constexpr int kHistBins = 4096;   // first radix digit: order-key bits 31..20
 constexpr int kMaxTopK = 4096;
-constexpr int kMaxChunks = 4096;  // top-k chunks per query (LDS arrays of the resolver)
-constexpr int kCandCap = 16384;   // candidates kept per query before the slow path
+constexpr int kMaxChunks = 1024;  // top-k chunks per query (LDS arrays of k_emit)
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
 constexpr int kMaxSplitRows = 2048;  // selected rows per attention work-group
 
@@ -29,32 +28,22 @@ struct Plan {
     int64_t score_ld;             // row stride of the workspace score matrix
     int32_t chunk;                // rows per top-k chunk
     int32_t n_chunks;             // chunks per query
-    int32_t cand_cap;             // candidate slots per query
+    int32_t cand_cap;             // candidate slots per chunk
     int32_t sel_max;              // top_k + kpool - 1
     int32_t split_rows;           // selected rows per attention work-group
     int32_t n_split;              // attention splits per query
     int32_t score_tile;           // key rows per score work-group
 
     // workspace byte offsets; [0, ctrl_bytes) must be zero between calls
-    size_t off_hist, off_candn, off_done, ctrl_bytes;
-    size_t off_thr, off_chunk, off_cand, off_scores, off_sel, off_cnt;
+    size_t off_hist, ctrl_bytes;
+    size_t off_chunk, off_cand, off_scores, off_sel, off_cnt;
     size_t off_pacc, off_pml, total;
-};
-
-// Per-query result of the threshold search.
-struct Threshold {
-    uint32_t key;      // order key of the k-th ranked row
-    uint32_t mode;     // 0: dense (keep all), 1: sparse, 2: invalid query
-    uint32_t n_rows;   // rows(q) of a valid query
-    uint32_t n_vis;
 };
 
 // Per-(query, chunk) bookkeeping of the selection.
 struct ChunkInfo {
     uint32_t gt;       // rows whose first digit exceeds the threshold bucket
-    uint32_t off;      // output position of the chunk's first selected row
-    uint32_t eq_take;  // rows equal to the threshold that this chunk keeps
-    uint32_t pad;
+    uint32_t n_cand;   // rows in the threshold bucket (may exceed the slots)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -80,7 +69,7 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     while ((p.max_rows + ch - 1) / ch > kMaxChunks) ch <<= 1;
     p.chunk = (int32_t)ch;
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
-    p.cand_cap = (int32_t)(p.max_rows < kCandCap ? p.max_rows : kCandCap);
+    p.cand_cap = p.chunk / 4;     // a chunk's bucket rows beyond this take the slow path
 
     // attention splits: aim at ~128 (query, split) pairs = 512 work-groups of
     // 16 heads, whole 32-row steps, 64..kMaxSplitRows rows per split
@@ -98,12 +87,9 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
 
     size_t o = 0;
     p.off_hist = o;   o += align256((size_t)n_q * kHistBins * 4);
-    p.off_candn = o;  o += align256((size_t)n_q * 4);
-    p.off_done = o;   o += align256((size_t)n_q * 4);
     p.ctrl_bytes = o;
-    p.off_thr = o;    o += align256((size_t)n_q * sizeof(Threshold));
     p.off_chunk = o;  o += align256((size_t)n_q * p.n_chunks * sizeof(ChunkInfo));
-    p.off_cand = o;   o += align256((size_t)n_q * p.cand_cap * 8);
+    p.off_cand = o;   o += align256((size_t)n_q * p.n_chunks * p.cand_cap * 8);
     p.off_scores = o; o += align256((size_t)n_q * p.score_ld * 4);
     p.off_sel = o;    o += align256((size_t)n_q * p.sel_max * 4);
     p.off_cnt = o;    o += align256((size_t)n_q * 4);

@@ -80,8 +80,9 @@ def test_decode_step_matches_oracle(case):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, name)
     check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, name)
-    # the histograms the call used are back to zero (workspace contract)
-    hist_bytes = w.n_q * 2048 * 4
+    # the histogram the call used is back to zero (workspace contract): one
+    # 4096-bin histogram per query leads the workspace
+    hist_bytes = w.n_q * 4096 * 4
     assert int(dw.ws[:hist_bytes].count_nonzero()) == 0, f"{name}: histogram left dirty"
     # a second call on the same workspace gives the same result bit for bit
     out1, sel1 = dw.out.clone(), dw.sel.clone()
