@@ -31,6 +31,7 @@ struct Args {
     float *out, *lse;
     // workspace
     uint32_t *hist;
+    uint32_t *thr;        // per query: order key of the keep-th row
     ChunkInfo *chunks;
     uint64_t *cand;
     float *pacc, *pml;

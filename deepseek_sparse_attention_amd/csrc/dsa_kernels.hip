@@ -74,21 +74,28 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive prefix sum over a wave with DPP: Hillis-Steele shifts inside
+// each 16-lane row, then row_bcast:15 / row_bcast:31 carry the row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 // Exclusive prefix sum over a 256-thread block; smem needs 4 words.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *smem, uint32_t &total) {
     const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= (uint32_t)o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) smem[w] = x;
     __syncthreads();
-    uint32_t base = 0;
-    for (uint32_t i = 0; i < w; i++) base += smem[i];
-    total = smem[0] + smem[1] + smem[2] + smem[3];
+    const uint32_t s0 = smem[0], s1 = smem[1], s2 = smem[2], s3 = smem[3];
     __syncthreads();
+    total = s0 + s1 + s2 + s3;
+    const uint32_t base = (w > 0 ? s0 : 0u) + (w > 1 ? s1 : 0u) + (w > 2 ? s2 : 0u);
     return base + x - v;
 }
 
@@ -98,30 +105,39 @@ __device__ uint32_t block_sum(uint32_t v, uint32_t *smem) {
     return total;
 }
 
-// Radix step: with hist[0..nbins) of the items still in play and `need` of
+// Radix step: with hist[0..NB) of the items still in play and `need` of
 // them still to take from the top, find the bin b holding the need-th
 // largest: suffix(b) >= need > suffix(b+1).  Returns b, sets above =
-// suffix(b+1).  nbins is 2048 or 1024; 256 threads.
-__device__ uint32_t find_bucket(const uint32_t *hist, int nbins, uint32_t need, uint32_t *smem,
-                                uint32_t *res, uint32_t &above) {
-    const int per = nbins / 256;
-    // thread t owns bins [nbins - per*(t+1), nbins - per*t): descending order
-    const int hi = nbins - per * (int)threadIdx.x;
+// suffix(b+1).  256 threads; thread t owns the PER bins just below
+// NB - PER*t, kept in registers.
+template <int NB>
+__device__ uint32_t find_bucket(const uint32_t *hist, uint32_t need, uint32_t *smem, uint32_t *res,
+                                uint32_t &above) {
+    constexpr int PER = NB / 256;
+    const int hi = NB - PER * (int)threadIdx.x;
+    uint32_t c[PER];
     uint32_t s = 0;
-    for (int i = 1; i <= per; i++) s += hist[hi - i];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        c[i] = hist[hi - 1 - i];
+        s += c[i];
+    }
     uint32_t total;
-    uint32_t before = block_excl_scan(s, smem, total);   // items in higher bins
+    const uint32_t before = block_excl_scan(s, smem, total);   // items in higher bins
     if (before < need && before + s >= need) {
-        uint32_t run = before;
-        for (int i = 1; i <= per; i++) {
-            const uint32_t c = hist[hi - i];
-            if (run + c >= need) {
-                res[0] = (uint32_t)(hi - i);
-                res[1] = run;
-                break;
+        uint32_t run = before, bin = 0, run_at = 0;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            if (!found && run + c[i] >= need) {
+                found = true;
+                bin = (uint32_t)(hi - 1 - i);
+                run_at = run;
             }
-            run += c;
+            run += c[i];
         }
+        res[0] = bin;
+        res[1] = run_at;
     }
     __syncthreads();
     above = res[1];
@@ -273,14 +289,12 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
 //   k_filter (grid chunks x queries): from the first-digit histogram find the
 //     bucket b1 holding the keep-th row; count the chunk's rows above b1 and
 //     copy the bucket's rows (key, row) into the chunk's own candidate slots.
-//   k_emit (same grid): every work-group gathers all candidates of its query
-//     into LDS, resolves the exact threshold from them (second and third
-//     digit), derives its chunk's output offset and its share of the rows
-//     equal to the threshold (lowest chunks first), then writes its
-//     selected rows in ascending order.
-// No global atomics: chunks own their candidate slots; if a chunk's bucket
-// rows overflow them, or all candidates overflow the LDS copy, k_emit
-// derives the candidates from the scores instead (slow, exact).
+//   k_resolve (one work-group per query): gathers all candidates into LDS,
+//     resolves the exact threshold (second and third digit) and each
+//     chunk's output offset and share of the rows equal to the threshold.
+//   k_emit (chunks x queries): writes each chunk's selected rows in
+//     ascending order at the chunk's offset.
+// No global atomics: chunks own their candidate slots.
 
 __device__ __forceinline__ void load_hist(const uint32_t *gh, uint32_t *lh) {
     uint32_t v[kHistBins / 256];
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     load_hist(a.hist + (size_t)q * kHistBins, hist);
     __syncthreads();
     uint32_t n_gt1;
-    const uint32_t b1 = find_bucket(hist, kHistBins, (uint32_t)a.keep, scan, res, n_gt1);
+    const uint32_t b1 = find_bucket<kHistBins>(hist, (uint32_t)a.keep, scan, res, n_gt1);
 
     uint64_t *slots = a.cand + ((size_t)q * a.n_chunks + c) * a.cand_cap;
     uint32_t gt = 0, n_cand = 0;
@@ -359,67 +373,73 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     }
 }
 
-constexpr int kLdsCand = 6144;   // candidates k_emit keeps in LDS
+constexpr int kLdsCand = 8192;   // candidates k_resolve keeps in LDS
 
-struct EmitShared {
+struct ResolveShared {
     uint32_t h[kHistBins];        // first digit, then the second (1024 bins)
     uint32_t h3[1024];            // third digit
     uint32_t pre[kMaxChunks + 1]; // exclusive prefix of the chunks' candidate counts
+    uint32_t gtc[kMaxChunks];     // per chunk: bucket rows above the threshold
+    uint32_t eqc[kMaxChunks];     // per chunk: rows equal to the threshold
     uint64_t cand[kLdsCand];
     uint32_t scan[8];
     uint32_t res[4];
 };
 
-// grid (n_chunks, n_q), 256 threads; each thread takes 4 consecutive rows
-// per 1024-row step of its chunk.
-__global__ __launch_bounds__(256) void k_emit(Args a) {
-    __shared__ EmitShared sh;
-    const int q = blockIdx.y, c = blockIdx.x;
+// One work-group per sparse query: gathers the candidates of all chunks
+// into LDS, finds the second and third digits of the keep-th key (the
+// threshold), and writes each chunk's output offset and its share of the
+// rows equal to the threshold (lowest chunks first).  grid (n_q), 256
+// threads.  If some chunk's bucket rows overflowed its slots, or all of
+// them overflow the LDS copy, the bucket rows are re-derived from the
+// scores (slow, exact).
+__global__ __launch_bounds__(256) void k_resolve(Args a) {
+    __shared__ ResolveShared sh;
+    const int q = blockIdx.x;
     const QInfo qi = query_info(a, q);
-    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
-    if (qi.mode != 1) {
-        if (c != 0) return;
-        const int32_t cnt = qi.mode == 0 ? qi.nvis : 0;
-        for (int i = threadIdx.x; i < a.sel_ld; i += 256) dst[i] = i < cnt ? i : -1;
-        if (threadIdx.x == 0) a.sel_count[q] = cnt;
-        return;
-    }
+    if (qi.mode != 1) return;
     const int64_t rows = qi.rows;
     const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-    if (c >= nch) return;
     const uint32_t keep = (uint32_t)a.keep;
     const float *s = a.scores_in + (size_t)q * a.score_ld;
-    const ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
+    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
     const uint64_t *slots = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
     const uint32_t ch = (uint32_t)a.chunk;
 
-    // per-chunk counts: rows above the first-digit bucket before this chunk,
-    // and the candidate layout (each chunk's slots are packed in LDS)
-    uint32_t gt1_before = 0, my_nc = 0;
-    bool overflow = false;
     const int per = (nch + 255) / 256;
     const int c0 = threadIdx.x * per;
-    for (int i = c0; i < c0 + per && i < nch; i++) {
-        const ChunkInfo info = ci[i];
-        if (i < c) gt1_before += info.gt;
-        overflow |= info.n_cand > (uint32_t)a.cand_cap;
-        my_nc += info.n_cand < (uint32_t)a.cand_cap ? info.n_cand : (uint32_t)a.cand_cap;
+    uint32_t ncs[kMaxChunks / 256], gts[kMaxChunks / 256];
+    uint32_t my_nc = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks / 256; j++) {
+        ncs[j] = gts[j] = 0;
+        if (j < per && c0 + j < nch) {
+            const ChunkInfo info = ci[c0 + j];
+            gts[j] = info.gt;
+            overflow |= info.n_cand > (uint32_t)a.cand_cap;
+            ncs[j] = info.n_cand < (uint32_t)a.cand_cap ? info.n_cand : (uint32_t)a.cand_cap;
+            my_nc += ncs[j];
+        }
     }
     load_hist(a.hist + (size_t)q * kHistBins, sh.h);
     uint32_t n_all;
     uint32_t run = block_excl_scan(my_nc, sh.scan, n_all);
-    for (int i = c0; i < c0 + per && i < nch; i++) {
-        sh.pre[i] = run;
-        const uint32_t n = ci[i].n_cand;
-        run += n < (uint32_t)a.cand_cap ? n : (uint32_t)a.cand_cap;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks / 256; j++) {
+        if (j < per && c0 + j < nch) {
+            sh.pre[c0 + j] = run;
+            sh.gtc[c0 + j] = 0;
+            sh.eqc[c0 + j] = 0;
+            run += ncs[j];
+        }
     }
     if (threadIdx.x == 0) sh.pre[nch] = n_all;
     overflow = __syncthreads_or(overflow) || n_all > (uint32_t)kLdsCand;
     uint32_t n_gt1;
-    const uint32_t b1 = find_bucket(sh.h, kHistBins, keep, sh.scan, sh.res, n_gt1);
+    const uint32_t b1 = find_bucket<kHistBins>(sh.h, keep, sh.scan, sh.res, n_gt1);
     const uint32_t need1 = keep - n_gt1;
 
-    // all candidates into LDS (rounds of 16 per thread), second digit
     uint32_t *h2 = sh.h;
     __syncthreads();
     for (int i = threadIdx.x; i < 1024; i += 256) {
@@ -428,6 +448,7 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
     }
     __syncthreads();
     if (!overflow) {
+        // candidates of all chunks packed into LDS, 16 loads per thread a round
         for (uint32_t base = 0; base < n_all; base += 16 * 256) {
             uint64_t e[16];
 #pragma unroll
@@ -461,15 +482,12 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
     }
     __syncthreads();
     uint32_t n_gt2;
-    const uint32_t b2 = find_bucket(h2, 1024, need1, sh.scan, sh.res, n_gt2);
+    const uint32_t b2 = find_bucket<1024>(h2, need1, sh.scan, sh.res, n_gt2);
     const uint32_t need2 = need1 - n_gt2;
     const uint32_t pre2 = (b1 << 10) | b2;   // key >> 10 of the level-2 bucket
-    // third digit within the level-2 bucket; bucket rows of earlier chunks
-    // above the level-2 bucket are selected
-    uint32_t gt2_before = 0;
     auto pass3 = [&](uint32_t key, uint32_t r) {
         const uint32_t k10 = key >> 10;
-        if (k10 > pre2) gt2_before += (r / ch < (uint32_t)c) ? 1u : 0u;
+        if (k10 > pre2) atomicAdd(&sh.gtc[r / ch], 1u);
         else if (k10 == pre2) atomicAdd(&sh.h3[key & 0x3FF], 1u);
     };
     if (!overflow) {
@@ -482,14 +500,13 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
     }
     __syncthreads();
     uint32_t n_gt3;
-    const uint32_t b3 = find_bucket(sh.h3, 1024, need2, sh.scan, sh.res, n_gt3);
+    const uint32_t b3 = find_bucket<1024>(sh.h3, need2, sh.scan, sh.res, n_gt3);
     const uint32_t thr = (pre2 << 10) | b3;
     const uint32_t m_eq = need2 - n_gt3;     // rows equal to thr that are kept
-    uint32_t gt3_before = 0, eq_before = 0;
     auto pass4 = [&](uint32_t key, uint32_t r) {
-        if ((key >> 10) != pre2 || r / ch >= (uint32_t)c) return;
-        gt3_before += key > thr ? 1u : 0u;
-        eq_before += key == thr ? 1u : 0u;
+        if ((key >> 10) != pre2) return;
+        if (key > thr) atomicAdd(&sh.gtc[r / ch], 1u);
+        else if (key == thr) atomicAdd(&sh.eqc[r / ch], 1u);
     };
     if (!overflow) {
         for (uint32_t i = threadIdx.x; i < n_all; i += 256) pass4((uint32_t)(sh.cand[i] >> 32), (uint32_t)sh.cand[i]);
@@ -499,43 +516,100 @@ __global__ __launch_bounds__(256) void k_emit(Args a) {
             if ((key >> 20) == b1) pass4(key, (uint32_t)r);
         }
     }
-    const uint32_t before_gt = block_sum(gt1_before + gt2_before + gt3_before, sh.scan);
-    const uint32_t eq_b = block_sum(eq_before, sh.scan);
-    const uint32_t eq_taken = eq_b < m_eq ? eq_b : m_eq;
-    const uint32_t eq_take = m_eq - eq_taken;       // this chunk keeps its first eq_take equal rows
+    __syncthreads();
+    // equal rows go to the lowest chunks first; offsets are the exclusive
+    // prefix of each chunk's selected count
+    uint32_t eq_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks / 256; j++)
+        if (j < per && c0 + j < nch) eq_sum += sh.eqc[c0 + j];
+    uint32_t tot;
+    uint32_t eq_before = block_excl_scan(eq_sum, sh.scan, tot);
+    uint32_t takes[kMaxChunks / 256], sel_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks / 256; j++) {
+        takes[j] = 0;
+        if (j < per && c0 + j < nch) {
+            const uint32_t e = sh.eqc[c0 + j];
+            takes[j] = eq_before >= m_eq ? 0u : (m_eq - eq_before < e ? m_eq - eq_before : e);
+            eq_before += e;
+            sel_sum += gts[j] + sh.gtc[c0 + j] + takes[j];
+        }
+    }
+    uint32_t off = block_excl_scan(sel_sum, sh.scan, tot);
+#pragma unroll
+    for (int j = 0; j < kMaxChunks / 256; j++) {
+        if (j < per && c0 + j < nch) {
+            ci[c0 + j].off = off;
+            ci[c0 + j].eq_take = takes[j];
+            off += gts[j] + sh.gtc[c0 + j] + takes[j];
+        }
+    }
+    if (threadIdx.x == 0) a.thr[q] = thr;
+}
 
+// Writes the selection in ascending token order.  grid (n_chunks, n_q),
+// 256 threads; each thread takes 4 consecutive rows per 1024-row step.
+__global__ __launch_bounds__(256) void k_emit(Args a) {
+    __shared__ uint32_t scan[8];
+    const int q = blockIdx.y, c = blockIdx.x;
+    const QInfo qi = query_info(a, q);
+    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    if (qi.mode != 1) {
+        if (c != 0) return;
+        const int32_t cnt = qi.mode == 0 ? qi.nvis : 0;
+        for (int i = threadIdx.x; i < a.sel_ld; i += 256) dst[i] = i < cnt ? i : -1;
+        if (threadIdx.x == 0) a.sel_count[q] = cnt;
+        return;
+    }
+    const int64_t rows = qi.rows;
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    if (c >= nch) return;
+    const uint32_t keep = (uint32_t)a.keep;
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
     const int64_t r0 = (int64_t)c * a.chunk;
     const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+    float sv[4];
+    {
+        const int64_t rb = r0 + 4 * threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < 4; i++) sv[i] = rb + i < r1 ? s[rb + i] : 0.f;
+    }
+    const uint32_t thr = a.thr[q];
+    const ChunkInfo info = a.chunks[(size_t)q * a.n_chunks + c];
     const int kp = a.kpool;
-    uint32_t eq_base = 0, out_base = before_gt + eq_taken;
+    uint32_t eq_base = 0, out_base = info.off;
     for (int64_t base = r0; base < r1; base += 1024) {
         const int64_t rb = base + 4 * threadIdx.x;
-        uint32_t key[4];
+        if (base != r0) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) sv[i] = rb + i < r1 ? s[rb + i] : 0.f;
+        }
         bool gt[4], eq[4];
         uint32_t n_eq = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const bool ok = rb + i < r1;
-            key[i] = ok ? order_key(s[rb + i]) : 0u;
-            gt[i] = ok && key[i] > thr;
-            eq[i] = ok && key[i] == thr;
+            const uint32_t key = order_key(sv[i]);
+            gt[i] = ok && key > thr;
+            eq[i] = ok && key == thr;
             n_eq += eq[i];
         }
         uint32_t tot_eq;
-        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, sh.scan, tot_eq);
+        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, scan, tot_eq);
         bool take[4];
         uint32_t n_take = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             take[i] = gt[i];
             if (eq[i]) {
-                take[i] = eq_rank < eq_take;
+                take[i] = eq_rank < info.eq_take;
                 eq_rank++;
             }
             n_take += take[i];
         }
         uint32_t tot_take;
-        uint32_t pos = out_base + block_excl_scan(n_take, sh.scan, tot_take);
+        uint32_t pos = out_base + block_excl_scan(n_take, scan, tot_take);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             if (!take[i]) continue;
@@ -842,6 +916,11 @@ hipError_t launch_hist(const Args &a, hipStream_t st) {
 
 hipError_t launch_filter(const Args &a, hipStream_t st) {
     hipLaunchKernelGGL(k_filter, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_resolve, dim3(a.n_q), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

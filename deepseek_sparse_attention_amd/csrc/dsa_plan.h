@@ -36,7 +36,7 @@ struct Plan {
 
     // workspace byte offsets; [0, ctrl_bytes) must be zero between calls
     size_t off_hist, ctrl_bytes;
-    size_t off_chunk, off_cand, off_scores, off_sel, off_cnt;
+    size_t off_thr, off_chunk, off_cand, off_scores, off_sel, off_cnt;
     size_t off_pacc, off_pml, total;
 };
 
@@ -44,6 +44,8 @@ struct Plan {
 struct ChunkInfo {
     uint32_t gt;       // rows whose first digit exceeds the threshold bucket
     uint32_t n_cand;   // rows in the threshold bucket (may exceed the slots)
+    uint32_t off;      // output position of the chunk's first selected row
+    uint32_t eq_take;  // rows equal to the threshold that this chunk keeps
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,6 +90,7 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     size_t o = 0;
     p.off_hist = o;   o += align256((size_t)n_q * kHistBins * 4);
     p.ctrl_bytes = o;
+    p.off_thr = o;    o += align256((size_t)n_q * 4);
     p.off_chunk = o;  o += align256((size_t)n_q * p.n_chunks * sizeof(ChunkInfo));
     p.off_cand = o;   o += align256((size_t)n_q * p.n_chunks * p.cand_cap * 8);
     p.off_scores = o; o += align256((size_t)n_q * p.score_ld * 4);
