@@ -39,6 +39,7 @@ struct Args {
     int32_t chunk, n_chunks, cand_cap, split_rows, n_split, score_tile;
     int32_t fused;        // 1: dense queries are not scored, histogram accumulated
     int32_t clear_topk;   // 1: attention zeroes the top-k histogram
+    int32_t prefill;      // 1: runs of kPfQ queries share a sequence (dense contraction)
 };
 
 }  // namespace dsa

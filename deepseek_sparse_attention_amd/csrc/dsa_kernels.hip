@@ -49,6 +49,8 @@ __device__ __forceinline__ uint32_t order_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kPfQ = 8;          // queries per prefill work-group
+
 struct QInfo {
     int32_t seq, nvis, rows, mode;   // mode 0 dense, 1 sparse, 2 invalid
 };
@@ -66,6 +68,8 @@ __device__ __forceinline__ QInfo query_info(const Args &a, int q) {
     r.mode = (r.rows <= a.keep) ? 0 : 1;
     return r;
 }
+
+__device__ __forceinline__ int query_seq(const Args &a, int q) { return a.q_seq ? a.q_seq[q] : q; }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
@@ -166,6 +170,7 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
 // for k-step s.  D[head][row] lands as lane (g, n) holding heads 4g + r
 // (+16) of row n; the epilogue applies ReLU and the head weights and sums
 // the four lane groups.
+template <bool STRIDE>
 __global__ __launch_bounds__(256) void k_score(Args a) {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(16))) uint8_t tiles[4][64 * 256];
@@ -173,9 +178,9 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     const QInfo qi = query_info(a, q);
     if (qi.mode == 2) return;
     if (a.fused && qi.mode == 0) return;
-    const int64_t t0 = (int64_t)blockIdx.x * a.score_tile;
+    if (a.prefill && qi.seq == query_seq(a, q - q % kPfQ)) return;   // done by k_score_prefill
     const int64_t rows = qi.rows;
-    if (t0 >= rows) return;
+    if ((int64_t)blockIdx.x * a.score_tile >= rows) return;
     const bool hist = a.fused != 0;
     if (hist) {
         for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
@@ -200,8 +205,6 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     float *srow = a.scores + (size_t)q * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
     uint8_t *tb = tiles[w];
-    const int64_t end = t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
-
     u32x4 v[16];
     auto fetch = [&](int64_t base) {
 #pragma unroll
@@ -211,6 +214,11 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             v[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (lane & 15)));
         }
     };
+    // tiles t0 = blockIdx.x * tile, stepping by the grid (one pass in the
+    // common case; the prefill fix-up grid has one work-group per query)
+    for (int64_t t0 = (int64_t)blockIdx.x * a.score_tile; t0 < rows;
+         t0 = STRIDE ? t0 + (int64_t)gridDim.x * a.score_tile : rows) {
+    const int64_t end = t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
     int64_t base = t0 + 64 * w;
     if (base < end) fetch(base);
     for (; base < end; base += 256) {
@@ -254,11 +262,149 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             if (hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
         }
     }
+    }
     if (hist) {
         __syncthreads();
         uint32_t *gh = a.hist + (size_t)q * kHistBins;
         for (int i = threadIdx.x; i < kHistBins; i += 256)
             if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
+    }
+}
+
+// Chunked-prefill indexer: a dense [8 queries x 32 heads] x [128 x keys]
+// contraction per work-group.  grid (key ranges, query blocks of 8), 512
+// threads = 8 waves, wave w computes query 8*blockIdx.y + w.  The block's
+// queries are consecutive positions of one sequence (the leader's); a
+// query of another sequence is left to the fix-up pass of k_score.  Key
+// tiles of 128 rows are loaded with coalesced 16-byte loads (512 threads
+// x 4 = 32 KiB), staged swizzled in LDS (double buffer) and shared by the
+// eight queries; causality masks the scores and the histogram per query
+// (a query scores rows < rows(q)).  Per-query first-digit histograms live
+// in LDS as 16-bit counters, two to a word.
+constexpr int kPfTile = 128;     // key rows per LDS tile
+constexpr int kPfRange = 4096;   // key rows per work-group
+
+__global__ __launch_bounds__(512) void k_score_prefill(Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kPfTile * 256];
+    __shared__ uint32_t lh[kPfQ][kHistBins / 2];
+    __shared__ int32_t sh_rows[kPfQ];
+    const int w = threadIdx.x >> 6, lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int q0 = blockIdx.y * kPfQ;
+    const int q = q0 + w;
+    const int lead = query_seq(a, q0);
+    const bool hist = a.fused != 0;
+    // does this wave's query take part, and up to which row
+    if (lane == 0) {
+        int32_t rr = 0;
+        if (q < a.n_q) {
+            const QInfo qi = query_info(a, q);
+            const bool part = qi.mode != 2 && !(a.fused && qi.mode == 0) && qi.seq == lead;
+            rr = part ? qi.rows : 0;
+        }
+        sh_rows[w] = rr;
+    }
+    __syncthreads();
+    int32_t kmax = 0;
+#pragma unroll
+    for (int i = 0; i < kPfQ; i++) kmax = sh_rows[i] > kmax ? sh_rows[i] : kmax;
+    const int64_t k0 = (int64_t)blockIdx.x * kPfRange;
+    if (k0 >= kmax) return;
+    const int64_t k1 = k0 + kPfRange < kmax ? k0 + kPfRange : kmax;
+    const int32_t my_rows = sh_rows[w];
+    if (hist)
+        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) (&lh[0][0])[i] = 0;
+
+    bf16x8 qa[2][4];
+    float wt[2][4];
+    {
+        const int qq = q < a.n_q ? q : q0;
+        const uint16_t *qip = a.idx_q + (size_t)qq * kIdxHeads * kIdxDim;
+#pragma unroll
+        for (int mb = 0; mb < 2; mb++) {
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+                qa[mb][s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qip + (16 * mb + n) * kIdxDim + 32 * s + 8 * g));
+#pragma unroll
+            for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)qq * kIdxHeads + 16 * mb + 4 * g + r];
+        }
+    }
+    const uint8_t *K = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)lead * a.key_stride * kIdxDim);
+    float *srow = a.scores + (size_t)(q < a.n_q ? q : 0) * a.score_ld;
+    const int st_mine = 2 * (g & 1) + (g >> 1);
+
+    u32x4 v[4];
+    auto fetch = [&](int64_t base) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = threadIdx.x + 512 * i;        // 16-byte piece of the tile
+            int64_t r = base + (e >> 4);
+            r = r < kmax ? r : kmax - 1;
+            v[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (e & 15)));
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = threadIdx.x + 512 * i;
+            const int r = e >> 4, pc = e & 15;
+            *(u32x4 *)(&ktile[buf][r * 256 + 16 * (pc ^ (r & 7))]) = v[i];
+        }
+    };
+    fetch(k0);
+    int buf = 0;
+    for (int64_t base = k0; base < k1; base += kPfTile, buf ^= 1) {
+        stage(buf);
+        if (base + kPfTile < k1) fetch(base + kPfTile);
+        __syncthreads();
+        const uint8_t *tb = ktile[buf];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {                    // two groups of 64 keys
+            float p[4];
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+                const int r = 64 * j + 16 * st + n;
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], bv, acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], bv, acc1, 0, 0, 0);
+                }
+                float x = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
+                    x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
+                }
+                p[st] = x;
+            }
+            const bool b0 = g & 1, b1 = (g >> 1) & 1;
+            const float send0 = b0 ? p[0] : p[2], send1 = b0 ? p[1] : p[3];
+            const float keep0 = b0 ? p[2] : p[0], keep1 = b0 ? p[3] : p[1];
+            const float q0s = keep0 + __shfl_xor(send0, 16, 64);
+            const float q1s = keep1 + __shfl_xor(send1, 16, 64);
+            const float score = (b1 ? q1s : q0s) + __shfl_xor(b1 ? q0s : q1s, 32, 64);
+            const int64_t row = base + 64 * j + 16 * st_mine + n;
+            if (row < my_rows) {
+                srow[row] = score;
+                if (hist) {
+                    const uint32_t bin = order_key(score) >> 20;
+                    atomicAdd(&lh[w][bin >> 1], 1u << (16 * (bin & 1)));
+                }
+            }
+        }
+        __syncthreads();                                  // buffer free for the tile after next
+    }
+    if (hist) {
+        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) {
+            const int qq = q0 + i / (kHistBins / 2);
+            const uint32_t word = (&lh[0][0])[i];
+            if (!word || qq >= a.n_q) continue;
+            const int bin = 2 * (i % (kHistBins / 2));
+            uint32_t *gh = a.hist + (size_t)qq * kHistBins + bin;
+            if (word & 0xFFFFu) atomicAdd(gh, word & 0xFFFFu);
+            if (word >> 16) atomicAdd(gh + 1, word >> 16);
+        }
     }
 }
 
@@ -644,169 +790,242 @@ __device__ __forceinline__ void clear_topk_state(const Args &a, int q) {
 __global__ __launch_bounds__(256) void k_topk_clear(Args a) { clear_topk_state(a, blockIdx.x); }
 
 // ---------------------------------------------------------------- attention
-// One work-group = (query q, split sp, head group hg of 16 heads); 256
-// threads = 4 waves.  The split's selected rows are processed 32 at a time,
-// staged row-major in LDS (row stride D*2 + 32 bytes) with the next step's
-// rows already in flight in registers.  Per step:
-//   QK : S^T[row][head] = C Q^T; wave (b = w & 1, kh = w >> 1) multiplies
-//        row block b (16 rows) by its half of the k-steps, the two halves
-//        are added through LDS;
-//   softmax: online, per head (one head per lane column), lazy rescale
-//        (only when the running max grows by more than 2^8); every wave
-//        keeps the same running max so that all rescale alike;
-//   PV : O^T[col][head] += V^T P^T for the wave's 128 output columns, with
-//        A = V^T read by ds_read_b64_tr_b16 and B = P split into bf16 hi + lo.
-// Work-group ids are laid out so that the four head groups of one (q, sp)
-// are dispatched to the same XCD and read the gathered rows through one L2.
+// One work-group = (query q, split sp), all 64 heads, 512 threads = 8 waves.
+// Wave w = (head group hg = w & 3, half x = w >> 2): heads 16hg..16hg+15;
+// for the scores it covers half x of the D row dimensions, for the output
+// half x of the 512 latent columns.  The split's row indices are staged in
+// LDS first; its rows are then processed 32 at a time.  Rows reach LDS by
+// DMA (global_load_lds, no registers) through a ring of three buffers, two
+// steps ahead of the compute: the V part of a row (1 KiB) is one wave
+// instruction into a row-major region (stride 1056 B), the 64-wide RoPE
+// tail goes 8 rows per instruction into a region of 128-byte rows whose
+// 16-byte pieces are XOR-swizzled by (row & 7).  A missing row (past the
+// count, or an index outside the cache) is read from a zero row, so each
+// wave issues a fixed number of DMA instructions per step and the wait for
+// step c is an exact vmcnt.  Per step and wave:
+//   QK : partial S^T[row][head] = C Q^T over its half of the dimensions on
+//        MFMA 16x16x32 (A = rows from LDS, B = queries in registers), two
+//        16-row blocks; the two halves are summed through LDS;
+//   softmax: online per head (one head per lane column), lazy rescale
+//        when the running max grows by more than 2^8;
+//   PV : O^T[col][head] += V^T P^T for its 256 columns, A = V^T read by
+//        ds_read_b64_tr_b16, B = P split into bf16 hi + lo.
+// Two barriers per step: buffer ready, partial scores ready.
 template <int D>
 struct AttnCfg {
     static constexpr int ND = D / 32;            // MFMA k-steps of the score
     static constexpr int NH = ND / 2;            // k-steps per half
-    static constexpr int RS = D * 2 + 32;        // LDS row stride in bytes
-    static constexpr int PPR = D / 8;            // 16-byte pieces per row
-    static constexpr int PER = kAttnRows * PPR / 256;
+    static constexpr int VS = 1056;              // LDS stride of a V row (bytes)
+    static constexpr int VBYTES = kAttnRows * VS;
+    static constexpr int RBYTES = D > 512 ? kAttnRows * 128 : 0;
+    static constexpr int BUF = VBYTES + RBYTES;
+    static constexpr int NBUF = 3;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void k_attend(Args a) {
-    using Cfg = AttnCfg<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[kAttnRows * Cfg::RS];
-    __shared__ int32_t sidx[kMaxSplitRows];
-    __shared__ f32x4 sx[2][64];
-    __shared__ f32x4 pbuf[2][64];
-    __shared__ float bmax[2][16];
+// Source of the DMA for rows that do not exist.
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[2 * 576] = {};
 
-    const int n_pairs = a.n_q * a.n_split;
-    const int within = blockIdx.x & 31;
-    const int pair = (blockIdx.x >> 5) * 8 + (within & 7);
-    const int hg = within >> 3;
-    if (pair >= n_pairs) return;
-    const int q = pair / a.n_split, sp = pair % a.n_split;
-    if (a.clear_topk && sp == 0 && hg == 0) clear_topk_state(a, q);
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from src (per-lane address) to LDS at lds + 16 * lane.
+// Issued from asm so that the compiler's wait insertion, which knows
+// nothing of it, adds no vmcnt wait in front of the LDS reads of the other
+// buffers; the kernel waits for it itself.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS-only work-group barrier: global accesses in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void k_attend(Args a) {
+    using Cfg = AttnCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::NBUF * Cfg::BUF];
+    __shared__ int32_t sidx[kMaxSplitRows];
+    __shared__ f32x4 sx[8][2][64];                 // partial scores per wave
+    const int q = blockIdx.y, sp = blockIdx.x;
+    if (a.clear_topk && sp == 0) clear_topk_state(a, q);
     const QInfo qi = query_info(a, q);
-    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
-    const int b = w & 1, kh = w >> 1;
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hg = w & 3, x = w >> 2;
     const int head = 16 * hg + n;
 
+    // a count outside [0, top_k + kpool - 1] makes the query invalid
     int32_t count = 0;
-    if (qi.mode != 2) {
+    bool invalid = qi.mode == 2;
+    if (!invalid) {
         count = a.sel_count[q];
-        count = count < 0 ? 0 : (count > a.sel_ld ? a.sel_ld : count);
+        if (count < 0 || count > a.top_k + a.kpool - 1) {
+            invalid = true;
+            count = 0;
+        }
     }
     const int32_t start = sp * a.split_rows;
-    const int32_t nrows = (start + a.split_rows < count ? start + a.split_rows : count) - start;
-    const int32_t *selq = a.sel + (size_t)q * a.sel_ld;
-    for (int i = threadIdx.x; i < nrows; i += 256) {
-        int32_t t = selq[start + i];
-        sidx[i] = (t >= 0 && (int64_t)t < a.cache_stride) ? t : -1;
-    }
+    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
+    const int nst = (nrows + kAttnRows - 1) / kAttnRows;
+    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
 
+    // row indices of the split (-1: no row), padded to whole steps
+    {
+        const int32_t *selq = a.sel + (size_t)q * a.sel_ld + start;
+        for (int r = threadIdx.x; r < nst * kAttnRows; r += 512) {
+            int32_t t = -1;
+            if (r < nrows) {
+                t = selq[r];
+                if (t < 0 || (int64_t)t >= a.cache_stride) t = -1;
+            }
+            sidx[r] = t;
+        }
+    }
+    // this wave's queries: k-steps x*NH .. x*NH + NH - 1
     bf16x8 qreg[Cfg::NH];
     {
-        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 32 * Cfg::NH * kh;
+        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 32 * Cfg::NH * x + 8 * g;
 #pragma unroll
-        for (int s = 0; s < Cfg::NH; s++)
-            qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * s + 8 * g));
+        for (int j = 0; j < Cfg::NH; j++) qreg[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j));
+        // complete the query loads here: no load the compiler tracks may
+        // be in flight inside the loop, whose vmcnt waits count DMA only
+#pragma unroll
+        for (int j = 0; j < Cfg::NH; j++) asm volatile("" ::"v"(qreg[j]));
     }
-    f32x4 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY, l_part = 0.f;
-    const uint16_t *C = a.cache + (size_t)(qi.mode == 2 ? 0 : qi.seq) * a.cache_stride * D;
-    const int nch = (nrows + kAttnRows - 1) / kAttnRows;
     __syncthreads();
 
-    u32x4 v[Cfg::PER];
-    auto fetch = [&](int c) {
+    // DMA of step c's rows into buffer slot b: V parts of rows w, w+8,
+    // w+16, w+24; waves 0..3 also the RoPE tails of rows 8w..8w+7
+    const bool rope_wave = D > 512 && w < 4;
+    auto issue = [&](int c, int b) {
+        uint8_t *vb = lds + b * Cfg::BUF;
+        const int32_t *si = sidx + kAttnRows * c;
 #pragma unroll
-        for (int i = 0; i < Cfg::PER; i++) {
-            const int e = threadIdx.x + 256 * i;
-            const int rr = e / Cfg::PPR, pc = e % Cfg::PPR;
-            const int r = kAttnRows * c + rr;
-            const int32_t t = r < nrows ? sidx[r] : -1;
-            v[i] = t >= 0 ? *(const u32x4 *)(C + (size_t)t * D + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 4; i++) {
+            const int r = w + 8 * i;
+            const int32_t t = si[r];
+            const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
+            dma16(src + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(vb + r * Cfg::VS)));
+        }
+        if (rope_wave) {
+            const int row = 8 * w + (lane >> 3);
+            const int32_t t = si[row];
+            const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
+            const int piece = (lane & 7) ^ (row & 7);
+            dma16(src + 1024 + 16 * piece, __builtin_amdgcn_readfirstlane(lds_addr(vb + Cfg::VBYTES + 8 * w * 128)));
         }
     };
-    if (nch > 0) fetch(0);
 
-    for (int c = 0; c < nch; c++) {
-        if (c > 0) __syncthreads();                  // previous step's PV is done with rowbuf
+    f32x4 acc[16];
 #pragma unroll
-        for (int i = 0; i < Cfg::PER; i++) {
-            const int e = threadIdx.x + 256 * i;
-            const int rr = e / Cfg::PPR, pc = e % Cfg::PPR;
-            *(u32x4 *)(rowbuf + rr * Cfg::RS + 16 * pc) = v[i];
-        }
-        if (c + 1 < nch) fetch(c + 1);
-        __syncthreads();
+    for (int i = 0; i < 16; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_part = 0.f;
 
-        // QK: this wave's row block and half of the k-steps
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+    if (nst > 0) issue(0, 0);
+    if (nst > 1) issue(1, 1);
+    int b_cur = 0;
+    for (int c = 0; c < nst; c++) {
+        // this wave's DMA of step c is done (step c + 1's may be in flight),
+        // then every wave's is
+        if (c + 1 < nst) {
+            if (rope_wave)
+                wait_vm<5>();
+            else
+                wait_vm<4>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();
+        if (c + 2 < nst) issue(c + 2, b_cur == 0 ? 2 : b_cur - 1);
+        const uint8_t *vb = lds + b_cur * Cfg::BUF;
+        b_cur = b_cur == 2 ? 0 : b_cur + 1;
+        const uint64_t okmask = __ballot(lane < kAttnRows && sidx[kAttnRows * c + (lane & 31)] >= 0);
+
+        // partial S^T over this wave's half of the dimensions
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         {
-            const uint8_t *rp = rowbuf + (16 * b + n) * Cfg::RS + 64 * Cfg::NH * kh + 16 * g;
+            // all A operands first (one LDS latency for the step), then
+            // the MFMA chains of the two row blocks
+            const int sb = Cfg::NH * x;
+            bf16x8 ra[2 * Cfg::NH];
 #pragma unroll
-            for (int s = 0; s < Cfg::NH; s++) {
-                bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rp + 64 * s));
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[s], sa, 0, 0, 0);
+            for (int j = 0; j < Cfg::NH; j++) {
+                const int s = sb + j;
+                const uint8_t *p0, *p1;
+                if (D > 512 && s >= 16) {
+                    const int pc = 4 * (s - 16) + g;
+                    p0 = vb + Cfg::VBYTES + n * 128 + 16 * (pc ^ (n & 7));
+                    p1 = vb + Cfg::VBYTES + (16 + n) * 128 + 16 * (pc ^ (n & 7));
+                } else {
+                    p0 = vb + n * Cfg::VS + 64 * s + 16 * g;
+                    p1 = vb + (16 + n) * Cfg::VS + 64 * s + 16 * g;
+                }
+                ra[2 * j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)p0);
+                ra[2 * j + 1] = __builtin_bit_cast(bf16x8, *(const u32x4 *)p1);
             }
-        }
-        if (kh == 1) sx[b][lane] = sa;
-        __syncthreads();
-        float z[4];
-        if (kh == 0) {
-            sa += sx[b][lane];
-            float bm = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = kAttnRows * c + 16 * b + 4 * g + r;
-                const bool ok = row < nrows && sidx[row] >= 0;
-                z[r] = ok ? sa[r] * a.scale_log2 : -INFINITY;
-                bm = fmaxf(bm, z[r]);
+            for (int j = 0; j < Cfg::NH; j++) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[2 * j], qreg[j], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[2 * j + 1], qreg[j], s1, 0, 0, 0);
             }
-            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            if (g == 0) bmax[b][n] = bm;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * Cfg::NH, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * Cfg::NH, 0);
         }
-        __syncthreads();
-        {
-            const float cmax = fmaxf(bmax[0][n], bmax[1][n]);
-            const bool need = cmax > m_ref + 8.f;
-            if (__any(need)) {
-                const float m_new = need ? cmax : m_ref;
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-                m_ref = m_new;
-                l_part *= alpha;
+        sx[w][0][lane] = s0;
+        sx[w][1][lane] = s1;
+        lds_barrier();
+        s0 += sx[w ^ 4][0][lane];
+        s1 += sx[w ^ 4][1][lane];
+
+        // online softmax over this step's rows, per head (lane column n);
+        // element j of this lane is row 4g + j (j < 4) or 16 + 4g + j - 4
+        float z[8];
+        float cmax = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 8; i++) acc[i] *= alpha;
-            }
+        for (int j = 0; j < 8; j++) {
+            const int rr = (j < 4 ? 0 : 16) + 4 * g + (j & 3);
+            const float sv = j < 4 ? s0[j] : s1[j - 4];
+            const float v = ((okmask >> rr) & 1) ? sv * a.scale_log2 : -INFINITY;
+            z[j] = v;
+            cmax = fmaxf(cmax, v);
         }
-        if (kh == 0) {
-            f32x4 p;
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        const bool need = cmax > m_ref + 8.f;
+        if (__any(need)) {
+            const float m_new = need ? cmax : m_ref;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+            m_ref = m_new;
+            l_part *= alpha;
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                p[r] = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-            pbuf[b][lane] = p;
+            for (int i = 0; i < 16; i++) acc[i] *= alpha;
         }
-        __syncthreads();
         bf16x8 phi, plo;
-        {
-            const f32x4 p0 = pbuf[0][lane], p1 = pbuf[1][lane];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float p = j < 4 ? p0[j] : p1[j - 4];
-                l_part += p;
-                const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
-                const float lo = p - __uint_as_float(hb);
-                phi[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
-                plo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(lo) >> 16));
-            }
+        for (int j = 0; j < 8; j++) {
+            const float p = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[j] - m_ref);
+            l_part += p;
+            const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
+            const float lo = p - __uint_as_float(hb);
+            phi[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+            plo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(lo) >> 16));
         }
+        // O^T += V^T P^T over this wave's 16 column blocks of 16
         {
             const int r_in = n >> 2, c_in = n & 3;
-            const uint8_t *v1 = rowbuf + (4 * g + r_in) * Cfg::RS + 256 * w + 8 * c_in;
-            const uint8_t *v2 = rowbuf + (16 + 4 * g + r_in) * Cfg::RS + 256 * w + 8 * c_in;
+            const uint8_t *v1 = vb + (4 * g + r_in) * Cfg::VS + 8 * c_in + 512 * x;
+            const uint8_t *v2 = vb + (16 + 4 * g + r_in) * Cfg::VS + 8 * c_in + 512 * x;
 #pragma unroll
-            for (int cb = 0; cb < 8; cb++) {
+            for (int cb = 0; cb < 16; cb++) {
                 const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v1 + 32 * cb));
                 const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v2 + 32 * cb));
                 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -815,31 +1034,41 @@ __global__ __launch_bounds__(256) void k_attend(Args a) {
                 acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, acc[cb], 0, 0, 0);
                 acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, acc[cb], 0, 0, 0);
             }
+            // V reads run 4 column blocks ahead of the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < 12; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
     }
     // total softmax mass per head over the four lane groups
     float l_tot = l_part + __shfl_xor(l_part, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
 
-    const int col0 = 128 * w + 4 * g;
+    const int col0 = 256 * x + 4 * g;
     if (a.n_split == 1) {
-        const bool bad = qi.mode == 2 || l_tot == 0.f;
+        const bool bad = invalid || l_tot == 0.f;
         const float inv = 1.f / l_tot;
         float *o = a.out + ((size_t)q * kHeads + head) * kLatent + col0;
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
+        for (int cb = 0; cb < 16; cb++) {
             f32x4 val = acc[cb] * inv;
             if (bad) val = f32x4{NAN, NAN, NAN, NAN};
             *(f32x4 *)(o + 16 * cb) = val;
         }
-        if (a.lse && w == 0 && g == 0)
+        if (a.lse && x == 0 && g == 0)
             a.lse[(size_t)q * kHeads + head] = bad ? NAN : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
     } else {
+        // an invalid query leaves m = -inf, l = 0 in every split: the merge
+        // then writes NaN
         const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + head;
         float *o = a.pacc + slot * kLatent + col0;
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) *(f32x4 *)(o + 16 * cb) = acc[cb];
-        if (w == 0 && g == 0) {
+        for (int cb = 0; cb < 16; cb++) *(f32x4 *)(o + 16 * cb) = acc[cb];
+        if (x == 0 && g == 0) {
             a.pml[2 * slot] = m_ref;
             a.pml[2 * slot + 1] = l_tot;
         }
@@ -904,8 +1133,19 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
 }
 
 hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
-    const unsigned tiles = (unsigned)((max_rows + a.score_tile - 1) / a.score_tile);
-    hipLaunchKernelGGL(k_score, dim3(tiles, a.n_q), dim3(256), 0, st, a);
+    if (a.prefill) {
+        const unsigned ranges = (unsigned)((max_rows + kPfRange - 1) / kPfRange);
+        hipLaunchKernelGGL(k_score_prefill, dim3(ranges, (a.n_q + kPfQ - 1) / kPfQ), dim3(512), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // in prefill mode k_score only picks up queries outside their block's
+    // sequence: one work-group per query, striding over the tiles
+    if (a.prefill)
+        hipLaunchKernelGGL(k_score<true>, dim3(1, a.n_q), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_score<false>, dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q),
+                           dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -935,12 +1175,10 @@ hipError_t launch_emit(const Args &a, hipStream_t st) {
 }
 
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between) {
-    // 4 head groups per (query, split); groups of 8 (query, split) pairs
-    const unsigned blocks = (unsigned)(((a.n_q * a.n_split + 7) / 8) * 32);
     if (a.D == 576)
-        hipLaunchKernelGGL(k_attend<576>, dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_attend<576>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
     else
-        hipLaunchKernelGGL(k_attend<512>, dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_attend<512>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (between) between();
     if (e != hipSuccess || a.n_split == 1) return e;

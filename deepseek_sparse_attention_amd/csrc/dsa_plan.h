@@ -16,7 +16,7 @@ constexpr int kHistBins = 4096;   // first radix digit: order-key bits 31..20
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxChunks = 1024;  // top-k chunks per query (LDS arrays of k_emit)
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
-constexpr int kMaxSplitRows = 2048;  // selected rows per attention work-group
+constexpr int kMaxSplitRows = 4096;  // selected rows per attention work-group
 
 // Everything a launch needs that depends on (geometry, n_q, max_nvis).
 struct Plan {
@@ -73,8 +73,9 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
     p.cand_cap = p.chunk / 4;     // a chunk's bucket rows beyond this take the slow path
 
-    // attention splits: aim at ~128 (query, split) pairs = 512 work-groups of
-    // 16 heads, whole 32-row steps, 64..kMaxSplitRows rows per split
+    // attention splits: aim at ~128 (query, split) work-groups (one CU
+    // each), whole 32-row steps, 64..kMaxSplitRows rows per split; the
+    // environment variable DSA_ATTN_PAIRS overrides the target (tuning)
     int64_t ns = (128 + n_q - 1) / n_q;
     if (const char *e = getenv("DSA_ATTN_PAIRS")) ns = (atoi(e) + n_q - 1) / n_q;
     int64_t sr = (p.sel_max + ns - 1) / ns;

@@ -47,8 +47,11 @@
  *    counts, selection indices) cannot be checked on the host.  Kernels treat
  *    a query whose sequence id is outside [0, n_seq) or whose visible count is
  *    outside [1, max_nvis] as invalid: it gets sel_count 0, no selection, and
- *    NaN output and lse.  Selection entries outside [0, cache rows) are
- *    skipped by the attention.  No such value causes an out-of-bounds access.
+ *    NaN output and lse.  Selection entries outside [0, cache_seq_stride)
+ *    are skipped by the attention; a sel_count outside
+ *    [0, top_k + kpool - 1] makes the attention of that query NaN, and a
+ *    query left with no row gets NaN too.  No such value causes an
+ *    out-of-bounds access.
  */
 #ifndef DSA_H
 #define DSA_H

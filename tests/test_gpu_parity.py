@@ -169,6 +169,76 @@ def test_attend_matches_oracle(d_rope, count):
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), out_ref, lse_ref, f"attend D={D} n={count}")
 
 
+def _attend_case(d_rope, n_q, sel, cnt, T, seed):
+    rng = np.random.default_rng(seed)
+    g = geom(kpool=4 if d_rope == 0 else 1, d_rope=d_rope)
+    D = 512 + d_rope
+    cache = I.f32_to_bf16_bits(rng.standard_normal((2, T, D)).astype(np.float32))
+    q = I.f32_to_bf16_bits(rng.standard_normal((n_q, 64, D)).astype(np.float32))
+    q_seq = (np.arange(n_q) % 2).astype(np.int32)
+    sel_ld = sel.shape[1]
+    dev = "cuda"
+    b = B.batch(torch.from_numpy(q_seq).to(dev), torch.full((n_q,), T, dtype=torch.int32, device=dev), T, 2)
+    ws = B.new_workspace(g, n_q, T)
+    out = torch.full((n_q, 64, 512), 7.0, device=dev)
+    lse = torch.full((n_q, 64), 7.0, device=dev)
+    B.mla_attend(g, b, torch.from_numpy(q).to(dev), torch.from_numpy(cache).to(dev), T,
+                 torch.from_numpy(sel).to(dev), sel_ld, torch.from_numpy(cnt).to(dev), out, lse, ws)
+    torch.cuda.synchronize()
+    return g, q_seq, q, cache, out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("d_rope", [64, 0])
+def test_attend_skips_invalid_rows_and_counts(d_rope):
+    """Entries outside [0, T) inside the count are skipped; a count outside
+    [0, top_k + kpool - 1], or one that leaves no row, gives NaN."""
+    log(f"attend edge rows d_rope={d_rope}")
+    rng = np.random.default_rng(91 + d_rope)
+    T, n_q = 3000, 8
+    kp = 4 if d_rope == 0 else 1
+    sel_ld = 2048 + kp - 1
+    sel = np.full((n_q, sel_ld), -1, np.int32)
+    cnt = np.zeros(n_q, np.int32)
+    for j in range(n_q):
+        c = [700, 1500, 40, 2048 + kp - 1, 64, 5, 10, 300][j]
+        sel[j, :c] = np.sort(rng.choice(T, c, replace=False))
+        cnt[j] = c
+    sel[0, [3, 100, 650]] = -1            # skipped
+    sel[1, [0, 777]] = [T + 5, 2 ** 30]   # beyond the cache rows: skipped
+    cnt[4] = sel_ld + 1                   # too many: NaN
+    cnt[5] = -3                           # negative: NaN
+    sel[6, :10] = -1                      # nothing left: NaN
+    cnt[7] = 0                            # empty: NaN
+    g, q_seq, q, cache, out, lse = _attend_case(d_rope, n_q, sel, cnt, T, 5 + d_rope)
+    for j in range(4):
+        rows = sel[j, :cnt[j]]
+        rows = rows[(rows >= 0) & (rows < T)]
+        s1 = np.full((1, sel_ld), -1, np.int32)
+        s1[0, :len(rows)] = rows
+        o_ref, l_ref = O.mla_attend(q_seq[j:j + 1], 512, d_rope, 1 / 16, q[j:j + 1], cache, s1,
+                                    np.array([len(rows)], np.int32))
+        check_attention(out[j:j + 1], lse[j:j + 1], o_ref, l_ref, f"edge q{j}")
+    for j in range(4, 8):
+        assert np.isnan(out[j]).all() and np.isnan(lse[j]).all(), f"query {j} should be NaN"
+
+
+def test_attend_single_split_path():
+    """Many queries: every query is one work-group that writes its output
+    directly (no split merge)."""
+    log("attend single split")
+    rng = np.random.default_rng(17)
+    T, n_q = 2500, 300
+    sel_ld = 2048
+    sel = np.full((n_q, sel_ld), -1, np.int32)
+    cnt = rng.integers(1, 97, n_q).astype(np.int32)
+    cnt[:3] = [1, 32, 96]
+    for j in range(n_q):
+        sel[j, :cnt[j]] = np.sort(rng.choice(T, cnt[j], replace=False))
+    g, q_seq, q, cache, out, lse = _attend_case(64, n_q, sel, cnt, T, 23)
+    o_ref, l_ref = O.mla_attend(q_seq, 512, 64, 1 / 16, q, cache, sel, cnt)
+    check_attention(out, lse, o_ref, l_ref, "single split")
+
+
 def test_prefill_chunk_small():
     """Chunked prefill at positions 0..511 of a 4096-token context: early
     queries keep all their candidates, later ones select."""
@@ -194,3 +264,30 @@ def test_prefill_chunk_sparse_small():
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, "prefill tail")
     check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, "prefill tail")
+
+
+def test_prefill_runs_with_mixed_sequences():
+    """Prefill batches (runs of 8 queries sharing a sequence) where one run
+    mixes sequences: the dense contraction covers the run leader's
+    sequence, the fix-up pass the others; both standalone and fused."""
+    log("prefill mixed runs")
+    T = 5000
+    q_seq = [0] * 8 + [1, 1, 0, 1, 1, 1, 0, 1] + [1] * 4
+    pos = [T - 20 + i for i in range(8)] + [4000 + 37 * i for i in range(8)] + [2100, 2200, 2300, 4999]
+    w = I.make_workload("pfm", 15, I.GEOM_TOKEN, 2, T, q_seq, [p + 1 for p in pos])
+    dw = DeviceWorkload(w)
+    dw.batch = B.batch(dw.q_seq, dw.q_nvis, dw.max_nvis, w.n_seq, 8)
+    ld = dw.max_nvis + 3
+    scores = torch.full((w.n_q, ld), float("nan"), device="cuda")
+    B.index_scores(w.geom, dw.batch, dw.idx_q, dw.idx_w, dw.idx_k, w.key_rows, scores, ld)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    ref = O.index_scores(w.q_seq, w.q_nvis, 1, w.idx_q, w.idx_w, w.idx_k, score_ld=ld)
+    got = scores.cpu().numpy()
+    for j in range(w.n_q):
+        rows = int(w.q_nvis[j])
+        assert np.array_equal(got[j, :rows], ref[j, :rows]), f"query {j}"
+        assert np.isnan(got[j, rows:]).all(), f"query {j} wrote past rows"
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, "prefill mixed")
+    check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, "prefill mixed")
