@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "DSA decode queries/sec at 128K ctx, top-k 2048; achieved HBM GB/s vs peak"
-KERNELS = ["score", "filter", "resolve", "emit", "attend", "merge"]
+KERNELS = ["score", "filter", "select", "attend", "merge"]
 
 
 def algorithmic_bytes(w):

@@ -22,9 +22,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st);
 hipError_t launch_hist(const Args &a, hipStream_t st);
 hipError_t launch_filter(const Args &a, hipStream_t st);
-hipError_t launch_resolve(const Args &a, hipStream_t st);
-hipError_t launch_topk_clear(const Args &a, hipStream_t st);
-hipError_t launch_emit(const Args &a, hipStream_t st);
+hipError_t launch_select(const Args &a, hipStream_t st);
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
 }  // namespace dsa
 
@@ -136,7 +134,7 @@ void bind_workspace(dsa::Args &a, const dsa::Plan &p, void *ws) {
     uint8_t *w = static_cast<uint8_t *>(ws);
     a.hist = reinterpret_cast<uint32_t *>(w + p.off_hist);
     a.thr = reinterpret_cast<uint32_t *>(w + p.off_thr);
-    a.chunks = reinterpret_cast<dsa::ChunkInfo *>(w + p.off_chunk);
+    a.chunk_cnt = reinterpret_cast<uint32_t *>(w + p.off_chunk);
     a.cand = reinterpret_cast<uint64_t *>(w + p.off_cand);
     a.pacc = reinterpret_cast<float *>(w + p.off_pacc);
     a.pml = reinterpret_cast<float *>(w + p.off_pml);
@@ -257,9 +255,7 @@ int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int
         a.sel_count = sel_count;
         DSA_TRY(launched(dsa::launch_hist(a, stream), "hist"));
         DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
-        DSA_TRY(launched(dsa::launch_resolve(a, stream), "resolve"));
-        DSA_TRY(launched(dsa::launch_emit(a, stream), "emit"));
-        return launched(dsa::launch_topk_clear(a, stream), "clear");
+        return launched(dsa::launch_select(a, stream), "select");
     });
 }
 
@@ -338,15 +334,12 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
         a.out = out;
         a.lse = lse;
         a.fused = 1;
-        a.clear_topk = 1;
         Timer tm(stream);
         DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream), "score"));
         tm.tick();
         DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
         tm.tick();
-        DSA_TRY(launched(dsa::launch_resolve(a, stream), "resolve"));
-        tm.tick();
-        DSA_TRY(launched(dsa::launch_emit(a, stream), "emit"));
+        DSA_TRY(launched(dsa::launch_select(a, stream), "select"));
         tm.tick();
         DSA_TRY(launched(dsa::launch_attend(a, stream, [&] { tm.tick(); }), "attend"));
         tm.tick();

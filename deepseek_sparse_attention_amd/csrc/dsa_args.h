@@ -31,14 +31,13 @@ struct Args {
     float *out, *lse;
     // workspace
     uint32_t *hist;
-    uint32_t *thr;        // per query: order key of the keep-th row
-    ChunkInfo *chunks;
+    uint32_t *thr;        // per query: first digit of the threshold, rows above its bucket
+    uint32_t *chunk_cnt;  // per (query, chunk): candidates found by k_filter
     uint64_t *cand;
     float *pacc, *pml;
     // plan
     int32_t chunk, n_chunks, cand_cap, split_rows, n_split, score_tile;
     int32_t fused;        // 1: dense queries are not scored, histogram accumulated
-    int32_t clear_topk;   // 1: attention zeroes the top-k histogram
     int32_t prefill;      // 1: runs of kPfQ queries share a sequence (dense contraction)
 };
 

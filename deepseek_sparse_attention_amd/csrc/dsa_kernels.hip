@@ -16,16 +16,19 @@
 //    TensorSharp2 "The block".
 //
 // Design (gfx950): the indexer is a [32 x 128] x [128 x rows] product per
-// query, issued on MFMA with the key rows streamed straight from HBM into the
-// B operand; its epilogue applies ReLU and the head weights and feeds a
-// 2048-bin histogram of the scores' order keys.  Top-k is an exact radix
-// select: the histogram fixes the threshold bucket, one pass collects that
-// bucket's candidates, the last work-group of each query resolves the exact
-// threshold and each chunk's output offset, and a final pass emits indices
-// in ascending order.  Attention gathers the selected rows into LDS, computes
-// S^T = C Q^T on MFMA, keeps an online softmax in fp32, and computes
-// O^T = V^T P^T on MFMA with V read through ds_read_b64_tr_b16 and P split
-// into two bf16 halves (hi + lo) so that P carries ~16 mantissa bits.
+// query on MFMA, key rows staged through LDS with coalesced loads (for a
+// prefill chunk, eight consecutive queries share each key tile); its
+// epilogue applies ReLU and the head weights and feeds a 4096-bin histogram
+// of the scores' order keys.  Top-k is an exact radix select: the histogram
+// fixes the threshold bucket, a pass over each chunk copies the rows at or
+// above it, in row order, into the chunk's slots, and one work-group per
+// query resolves the exact threshold from those candidates and writes the
+// kept rows in ascending order.  Attention streams the selected rows into
+// LDS by DMA, computes S^T = C Q^T on MFMA, keeps an online softmax in
+// fp32, and computes O^T = V^T P^T on MFMA with V read through
+// ds_read_b64_tr_b16 and P split into two bf16 halves (hi + lo) so that P
+// carries ~16 mantissa bits; split partials are merged by an LSE reduction.
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -430,16 +433,19 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
 
 // ---------------------------------------------------------------- top-k
 // Exact radix select over 32-bit order keys, ranked by (key descending,
-// row ascending), three digits: bits 31..20 (4096-bin histogram from the
-// score kernel or k_hist), bits 19..10 and bits 9..0.
-//   k_filter (grid chunks x queries): from the first-digit histogram find the
-//     bucket b1 holding the keep-th row; count the chunk's rows above b1 and
-//     copy the bucket's rows (key, row) into the chunk's own candidate slots.
-//   k_resolve (one work-group per query): gathers all candidates into LDS,
-//     resolves the exact threshold (second and third digit) and each
-//     chunk's output offset and share of the rows equal to the threshold.
-//   k_emit (chunks x queries): writes each chunk's selected rows in
-//     ascending order at the chunk's offset.
+// row ascending), three digits: d1 = bits 31..20 (4096-bin histogram from
+// the score kernel or k_hist), d2 = bits 19..10, d3 = bits 9..0.
+//   k_filter (grid chunks x queries): from the first-digit histogram find
+//     the bucket b1 holding the keep-th row; copy every row of the chunk
+//     whose d1 is at least b1 as (key, row) into the chunk's own candidate
+//     slots, in row order, and record how many there were.
+//   k_select (one work-group per query): gathers the candidates of all
+//     chunks into LDS in row order (re-reading the scores of a chunk whose
+//     slots overflowed), resolves d2 and d3 of the threshold there, and
+//     writes the kept rows in ascending order, expanded for pools, then the
+//     unpooled tail and -1 padding.  If the candidates do not fit in LDS it
+//     makes the same decisions from passes over the scores.  It also zeroes
+//     the query's histogram, the only state that must be zero between calls.
 // No global atomics: chunks own their candidate slots.
 
 __device__ __forceinline__ void load_hist(const uint32_t *gh, uint32_t *lh) {
@@ -450,7 +456,27 @@ __device__ __forceinline__ void load_hist(const uint32_t *gh, uint32_t *lh) {
     for (int i = 0; i < kHistBins / 256; i++) lh[threadIdx.x + 256 * i] = v[i];
 }
 
-// grid (n_chunks, n_q), 256 threads.
+// n scores from s[r0..r0+n) (rows at or past r1 read as 0); 16-byte loads
+// when the run is aligned and whole.
+template <int N>
+__device__ __forceinline__ void load_scores(const float *s, int64_t r0, int64_t r1, bool vec, float (&v)[N]) {
+    if (vec && r0 + N <= r1) {
+#pragma unroll
+        for (int j = 0; j < N / 4; j++) {
+            const f32x4 t = *(const f32x4 *)(s + r0 + 4 * j);
+            v[4 * j] = t[0];
+            v[4 * j + 1] = t[1];
+            v[4 * j + 2] = t[2];
+            v[4 * j + 3] = t[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] = r0 + i < r1 ? s[r0 + i] : 0.f;
+    }
+}
+
+// grid (n_chunks, n_q), 256 threads; thread t takes rows sb + 8t .. 8t + 7
+// of each 2048-row block, so the block-ordered compaction keeps row order.
 __global__ __launch_bounds__(256) void k_filter(Args a) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t scan[8];
@@ -462,332 +488,359 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     const int nch = (int)((rows + a.chunk - 1) / a.chunk);
     if (c >= nch) return;
     const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
     const int64_t r0 = (int64_t)c * a.chunk;
     const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
     // first block of scores in flight while the threshold bucket is found
     float sv[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int64_t r = r0 + 256 * i + threadIdx.x;
-        sv[i] = r < r1 ? s[r] : 0.f;
-    }
+    load_scores<8>(s, r0 + 8 * threadIdx.x, r1, vec, sv);
     load_hist(a.hist + (size_t)q * kHistBins, hist);
     __syncthreads();
-    uint32_t n_gt1;
-    const uint32_t b1 = find_bucket<kHistBins>(hist, (uint32_t)a.keep, scan, res, n_gt1);
+    uint32_t above1;
+    const uint32_t b1 = find_bucket<kHistBins>(hist, (uint32_t)a.keep, scan, res, above1);
+    if (c == 0 && threadIdx.x == 0) {
+        a.thr[2 * q] = b1;
+        a.thr[2 * q + 1] = above1;
+    }
 
     uint64_t *slots = a.cand + ((size_t)q * a.n_chunks + c) * a.cand_cap;
-    uint32_t gt = 0, n_cand = 0;
+    uint32_t n_cand = 0;
     for (int64_t sb = r0; sb < r1; sb += 2048) {
-        if (sb != r0) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int64_t r = sb + 256 * i + threadIdx.x;
-                sv[i] = r < r1 ? s[r] : 0.f;
-            }
-        }
+        const int64_t rb = sb + 8 * threadIdx.x;
+        if (sb != r0) load_scores<8>(s, rb, r1, vec, sv);
         uint32_t keys[8];
-        uint32_t n_c = 0;
+        uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int64_t r = sb + 256 * i + threadIdx.x;
-            const uint32_t key = order_key(sv[i]);
-            const bool ok = r < r1;
-            const uint32_t d1 = key >> 20;
-            gt += (ok && d1 > b1) ? 1u : 0u;
-            const bool is_c = ok && d1 == b1;
-            keys[i] = is_c ? key : 0u;
-            n_c += is_c ? 1u : 0u;
+            keys[i] = order_key(sv[i]);
+            if (rb + i < r1 && (keys[i] >> 20) >= b1) m |= 1u << i;
         }
         uint32_t tot;
-        uint32_t pos = n_cand + block_excl_scan(n_c, scan, tot);
+        uint32_t pos = n_cand + block_excl_scan(__builtin_popcount(m), scan, tot);
         n_cand += tot;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            if (!keys[i]) continue;      // order keys of real scores are never 0
-            const int64_t r = sb + 256 * i + threadIdx.x;
-            if (pos < (uint32_t)a.cand_cap) slots[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)r;
+            if (!((m >> i) & 1)) continue;
+            if (pos < (uint32_t)a.cand_cap) slots[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)(rb + i);
             pos++;
         }
     }
-    gt = block_sum(gt, scan);
-    if (threadIdx.x == 0) {
-        ChunkInfo info;
-        info.gt = gt;
-        info.n_cand = n_cand;
-        a.chunks[(size_t)q * a.n_chunks + c] = info;
-    }
+    if (threadIdx.x == 0) a.chunk_cnt[(size_t)q * a.n_chunks + c] = n_cand;
 }
 
-constexpr int kLdsCand = 8192;   // candidates k_resolve keeps in LDS
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelPer = 16;                       // rows per thread per pass tile
+constexpr int kSelTile = kSelThreads * kSelPer;
+constexpr int kSelCap = 12288;                    // candidates k_select keeps in LDS
 
-struct ResolveShared {
-    uint32_t h[kHistBins];        // first digit, then the second (1024 bins)
-    uint32_t h3[1024];            // third digit
-    uint32_t pre[kMaxChunks + 1]; // exclusive prefix of the chunks' candidate counts
-    uint32_t gtc[kMaxChunks];     // per chunk: bucket rows above the threshold
-    uint32_t eqc[kMaxChunks];     // per chunk: rows equal to the threshold
-    uint64_t cand[kLdsCand];
-    uint32_t scan[8];
-    uint32_t res[4];
+struct SelectShared {
+    uint32_t key[kSelCap];
+    int32_t row[kSelCap];
+    uint32_t pre[kMaxChunks + 1];  // exclusive prefix of the chunks' candidate counts
+    uint32_t h2[1024];
+    uint32_t h3[1024];
+    uint32_t tot[2][kSelWaves];
+    uint32_t res[2];
 };
 
-// One work-group per sparse query: gathers the candidates of all chunks
-// into LDS, finds the second and third digits of the keep-th key (the
-// threshold), and writes each chunk's output offset and its share of the
-// rows equal to the threshold (lowest chunks first).  grid (n_q), 256
-// threads.  If some chunk's bucket rows overflowed its slots, or all of
-// them overflow the LDS copy, the bucket rows are re-derived from the
-// scores (slow, exact).
-__global__ __launch_bounds__(256) void k_resolve(Args a) {
-    __shared__ ResolveShared sh;
-    const int q = blockIdx.x;
-    const QInfo qi = query_info(a, q);
-    if (qi.mode != 1) return;
-    const int64_t rows = qi.rows;
-    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-    const uint32_t keep = (uint32_t)a.keep;
-    const float *s = a.scores_in + (size_t)q * a.score_ld;
-    ChunkInfo *ci = a.chunks + (size_t)q * a.n_chunks;
-    const uint64_t *slots = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
-    const uint32_t ch = (uint32_t)a.chunk;
-
-    const int per = (nch + 255) / 256;
-    const int c0 = threadIdx.x * per;
-    uint32_t ncs[kMaxChunks / 256], gts[kMaxChunks / 256];
-    uint32_t my_nc = 0;
-    bool overflow = false;
-#pragma unroll
-    for (int j = 0; j < kMaxChunks / 256; j++) {
-        ncs[j] = gts[j] = 0;
-        if (j < per && c0 + j < nch) {
-            const ChunkInfo info = ci[c0 + j];
-            gts[j] = info.gt;
-            overflow |= info.n_cand > (uint32_t)a.cand_cap;
-            ncs[j] = info.n_cand < (uint32_t)a.cand_cap ? info.n_cand : (uint32_t)a.cand_cap;
-            my_nc += ncs[j];
-        }
-    }
-    load_hist(a.hist + (size_t)q * kHistBins, sh.h);
-    uint32_t n_all;
-    uint32_t run = block_excl_scan(my_nc, sh.scan, n_all);
-#pragma unroll
-    for (int j = 0; j < kMaxChunks / 256; j++) {
-        if (j < per && c0 + j < nch) {
-            sh.pre[c0 + j] = run;
-            sh.gtc[c0 + j] = 0;
-            sh.eqc[c0 + j] = 0;
-            run += ncs[j];
-        }
-    }
-    if (threadIdx.x == 0) sh.pre[nch] = n_all;
-    overflow = __syncthreads_or(overflow) || n_all > (uint32_t)kLdsCand;
-    uint32_t n_gt1;
-    const uint32_t b1 = find_bucket<kHistBins>(sh.h, keep, sh.scan, sh.res, n_gt1);
-    const uint32_t need1 = keep - n_gt1;
-
-    uint32_t *h2 = sh.h;
+// Exclusive prefix sum over the 1024 threads with one barrier; the 16-word
+// slot may be written again only after another barrier.
+__device__ __forceinline__ uint32_t sel_scan(uint32_t v, uint32_t *slot, uint32_t &total) {
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t x = wave_incl_scan(v);
+    if (lane == 63) slot[w] = x;
     __syncthreads();
-    for (int i = threadIdx.x; i < 1024; i += 256) {
-        h2[i] = 0;
-        sh.h3[i] = 0;
-    }
-    __syncthreads();
-    if (!overflow) {
-        // candidates of all chunks packed into LDS, 16 loads per thread a round
-        for (uint32_t base = 0; base < n_all; base += 16 * 256) {
-            uint64_t e[16];
+    uint32_t before = 0, tot = 0;
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const uint32_t i = base + 256 * j + threadIdx.x;
-                e[j] = 0;
-                if (i < n_all) {
-                    int lo = 0, hi = nch;          // chunk k with pre[k] <= i < pre[k+1]
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (sh.pre[mid] <= i) lo = mid;
-                        else hi = mid;
-                    }
-                    e[j] = slots[(size_t)lo * a.cand_cap + (i - sh.pre[lo])];
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const uint32_t i = base + 256 * j + threadIdx.x;
-                if (i < n_all) {
-                    sh.cand[i] = e[j];
-                    atomicAdd(&h2[(uint32_t)(e[j] >> 42) & 0x3FF], 1u);
-                }
-            }
-        }
-    } else {
-        for (int64_t r = threadIdx.x; r < rows; r += 256) {
-            const uint32_t key = order_key(s[r]);
-            if ((key >> 20) == b1) atomicAdd(&h2[(key >> 10) & 0x3FF], 1u);
-        }
+    for (int i = 0; i < kSelWaves; i++) {
+        const uint32_t t = slot[i];
+        before += i < (int)w ? t : 0u;
+        tot += t;
     }
-    __syncthreads();
-    uint32_t n_gt2;
-    const uint32_t b2 = find_bucket<1024>(h2, need1, sh.scan, sh.res, n_gt2);
-    const uint32_t need2 = need1 - n_gt2;
-    const uint32_t pre2 = (b1 << 10) | b2;   // key >> 10 of the level-2 bucket
-    auto pass3 = [&](uint32_t key, uint32_t r) {
-        const uint32_t k10 = key >> 10;
-        if (k10 > pre2) atomicAdd(&sh.gtc[r / ch], 1u);
-        else if (k10 == pre2) atomicAdd(&sh.h3[key & 0x3FF], 1u);
-    };
-    if (!overflow) {
-        for (uint32_t i = threadIdx.x; i < n_all; i += 256) pass3((uint32_t)(sh.cand[i] >> 32), (uint32_t)sh.cand[i]);
-    } else {
-        for (int64_t r = threadIdx.x; r < rows; r += 256) {
-            const uint32_t key = order_key(s[r]);
-            if ((key >> 20) == b1) pass3(key, (uint32_t)r);
-        }
-    }
-    __syncthreads();
-    uint32_t n_gt3;
-    const uint32_t b3 = find_bucket<1024>(sh.h3, need2, sh.scan, sh.res, n_gt3);
-    const uint32_t thr = (pre2 << 10) | b3;
-    const uint32_t m_eq = need2 - n_gt3;     // rows equal to thr that are kept
-    auto pass4 = [&](uint32_t key, uint32_t r) {
-        if ((key >> 10) != pre2) return;
-        if (key > thr) atomicAdd(&sh.gtc[r / ch], 1u);
-        else if (key == thr) atomicAdd(&sh.eqc[r / ch], 1u);
-    };
-    if (!overflow) {
-        for (uint32_t i = threadIdx.x; i < n_all; i += 256) pass4((uint32_t)(sh.cand[i] >> 32), (uint32_t)sh.cand[i]);
-    } else {
-        for (int64_t r = threadIdx.x; r < rows; r += 256) {
-            const uint32_t key = order_key(s[r]);
-            if ((key >> 20) == b1) pass4(key, (uint32_t)r);
-        }
-    }
-    __syncthreads();
-    // equal rows go to the lowest chunks first; offsets are the exclusive
-    // prefix of each chunk's selected count
-    uint32_t eq_sum = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxChunks / 256; j++)
-        if (j < per && c0 + j < nch) eq_sum += sh.eqc[c0 + j];
-    uint32_t tot;
-    uint32_t eq_before = block_excl_scan(eq_sum, sh.scan, tot);
-    uint32_t takes[kMaxChunks / 256], sel_sum = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxChunks / 256; j++) {
-        takes[j] = 0;
-        if (j < per && c0 + j < nch) {
-            const uint32_t e = sh.eqc[c0 + j];
-            takes[j] = eq_before >= m_eq ? 0u : (m_eq - eq_before < e ? m_eq - eq_before : e);
-            eq_before += e;
-            sel_sum += gts[j] + sh.gtc[c0 + j] + takes[j];
-        }
-    }
-    uint32_t off = block_excl_scan(sel_sum, sh.scan, tot);
-#pragma unroll
-    for (int j = 0; j < kMaxChunks / 256; j++) {
-        if (j < per && c0 + j < nch) {
-            ci[c0 + j].off = off;
-            ci[c0 + j].eq_take = takes[j];
-            off += gts[j] + sh.gtc[c0 + j] + takes[j];
-        }
-    }
-    if (threadIdx.x == 0) a.thr[q] = thr;
+    total = tot;
+    return before + x - v;
 }
 
-// Writes the selection in ascending token order.  grid (n_chunks, n_q),
-// 256 threads; each thread takes 4 consecutive rows per 1024-row step.
-__global__ __launch_bounds__(256) void k_emit(Args a) {
-    __shared__ uint32_t scan[8];
-    const int q = blockIdx.y, c = blockIdx.x;
+// Radix step over 1024 * PER bins; thread t holds the counts of bins
+// hi - 1 - i, hi = 1024 * PER - PER * t.  Finds the bin b with
+// suffix(b) >= need > suffix(b + 1); above = suffix(b + 1).
+template <int PER>
+__device__ uint32_t sel_find(const uint32_t (&c)[PER], uint32_t need, uint32_t *slot, uint32_t *res,
+                             uint32_t &above) {
+    const int hi = kSelThreads * PER - PER * (int)threadIdx.x;
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) s += c[i];
+    uint32_t total;
+    const uint32_t before = sel_scan(s, slot, total);
+    if (before < need && before + s >= need) {
+        uint32_t run = before, bin = 0, run_at = 0;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            if (!found && run + c[i] >= need) {
+                found = true;
+                bin = (uint32_t)(hi - 1 - i);
+                run_at = run;
+            }
+            run += c[i];
+        }
+        res[0] = bin;
+        res[1] = run_at;
+    }
+    __syncthreads();
+    above = res[1];
+    const uint32_t b = res[0];
+    __syncthreads();
+    return b;
+}
+
+// grid (n_q), 1024 threads.
+__global__ __launch_bounds__(kSelThreads) void k_select(Args a) {
+    __shared__ SelectShared sh;
+    const int q = blockIdx.x, tid = threadIdx.x;
     const QInfo qi = query_info(a, q);
     int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    {
+        uint32_t *gh = a.hist + (size_t)q * kHistBins;
+        for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+    }
     if (qi.mode != 1) {
-        if (c != 0) return;
         const int32_t cnt = qi.mode == 0 ? qi.nvis : 0;
-        for (int i = threadIdx.x; i < a.sel_ld; i += 256) dst[i] = i < cnt ? i : -1;
-        if (threadIdx.x == 0) a.sel_count[q] = cnt;
+        for (int i = tid; i < a.sel_ld; i += kSelThreads) dst[i] = i < cnt ? i : -1;
+        if (tid == 0) a.sel_count[q] = cnt;
         return;
     }
-    const int64_t rows = qi.rows;
-    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-    if (c >= nch) return;
-    const uint32_t keep = (uint32_t)a.keep;
-    const float *s = a.scores_in + (size_t)q * a.score_ld;
-    const int64_t r0 = (int64_t)c * a.chunk;
-    const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
-    float sv[4];
-    {
-        const int64_t rb = r0 + 4 * threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < 4; i++) sv[i] = rb + i < r1 ? s[rb + i] : 0.f;
-    }
-    const uint32_t thr = a.thr[q];
-    const ChunkInfo info = a.chunks[(size_t)q * a.n_chunks + c];
     const int kp = a.kpool;
-    uint32_t eq_base = 0, out_base = info.off;
-    for (int64_t base = r0; base < r1; base += 1024) {
-        const int64_t rb = base + 4 * threadIdx.x;
-        if (base != r0) {
+    const uint32_t keep = (uint32_t)a.keep;
+    const int64_t rows = qi.rows;
+    const float *s = a.scores_in + (size_t)q * a.score_ld;
+    const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+    const uint32_t b1 = a.thr[2 * q], above1 = a.thr[2 * q + 1];
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    int par = 0;                                    // alternates the scan slots
+
+    for (int i = tid; i < 1024; i += kSelThreads) {
+        sh.h2[i] = 0;
+        sh.h3[i] = 0;
+    }
+    // candidate counts per chunk -> row-ordered offsets
+    const uint32_t *cc = a.chunk_cnt + (size_t)q * a.n_chunks;
+    const uint32_t my_cnt = tid < nch ? cc[tid] : 0u;
+    uint32_t n_cand;
+    const uint32_t my_pre = sel_scan(my_cnt, sh.tot[par++ & 1], n_cand);
+    const bool any_ovf = __syncthreads_or(my_cnt > (uint32_t)a.cand_cap) != 0;
+    if (tid < nch) sh.pre[tid] = my_pre;
+    if (tid == 0) sh.pre[nch] = n_cand;
+    const bool in_lds = n_cand <= (uint32_t)kSelCap;
+    __syncthreads();
+
+    if (in_lds) {
+        // candidates of chunks whose slots held them all: wave w copies
+        // chunks w, w + 16, ..., four at a time, 128 candidates of each per
+        // round, every load issued before the stores
+        {
+            const int w = tid >> 6, lane = tid & 63;
+            for (int c0 = w; c0 < nch; c0 += 4 * kSelWaves) {
+                uint32_t cnt[4], base[4], mx = 0;
 #pragma unroll
-            for (int i = 0; i < 4; i++) sv[i] = rb + i < r1 ? s[rb + i] : 0.f;
+                for (int k = 0; k < 4; k++) {
+                    const int c = c0 + k * kSelWaves;
+                    cnt[k] = 0;
+                    base[k] = 0;
+                    if (c < nch) {
+                        base[k] = sh.pre[c];
+                        cnt[k] = sh.pre[c + 1] - base[k];
+                        if (cnt[k] > (uint32_t)a.cand_cap) cnt[k] = 0;   // re-scanned below
+                    }
+                    mx = cnt[k] > mx ? cnt[k] : mx;
+                }
+                for (uint32_t j0 = 0; j0 < mx; j0 += 128) {
+                    uint64_t v[4][2];
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+#pragma unroll
+                        for (int h = 0; h < 2; h++) {
+                            const uint32_t jj = j0 + 64 * h + lane;
+                            v[k][h] = jj < cnt[k]
+                                          ? a.cand[((size_t)q * a.n_chunks + c0 + k * kSelWaves) * a.cand_cap + jj]
+                                          : 0ull;
+                        }
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+#pragma unroll
+                        for (int h = 0; h < 2; h++) {
+                            const uint32_t jj = j0 + 64 * h + lane;
+                            if (jj < cnt[k]) {
+                                sh.key[base[k] + jj] = (uint32_t)(v[k][h] >> 32);
+                                sh.row[base[k] + jj] = (int32_t)(uint32_t)v[k][h];
+                            }
+                        }
+                }
+            }
         }
-        bool gt[4], eq[4];
+        // chunks whose slots overflowed: compact their rows again
+        for (int c = 0; any_ovf && c < nch; c++) {
+            const uint32_t cnt = sh.pre[c + 1] - sh.pre[c];
+            if (cnt <= (uint32_t)a.cand_cap) continue;
+            const int64_t r0 = (int64_t)c * a.chunk;
+            const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+            uint32_t base = sh.pre[c];
+            for (int64_t sb = r0; sb < r1; sb += kSelTile) {
+                const int64_t rb = sb + kSelPer * tid;
+                float v[kSelPer];
+                load_scores<kSelPer>(s, rb, r1, vec, v);
+                uint32_t keys[kSelPer];
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) {
+                    keys[i] = order_key(v[i]);
+                    if (rb + i < r1 && (keys[i] >> 20) >= b1) m |= 1u << i;
+                }
+                uint32_t tot;
+                uint32_t pos = base + sel_scan(__builtin_popcount(m), sh.tot[par++ & 1], tot);
+                base += tot;
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) {
+                    if (!((m >> i) & 1)) continue;
+                    if (pos < sh.pre[c + 1]) {
+                        sh.key[pos] = keys[i];
+                        sh.row[pos] = (int32_t)(rb + i);
+                    }
+                    pos++;
+                }
+            }
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < n_cand; i += kSelThreads) {
+            const uint32_t k = sh.key[i];
+            if ((k >> 20) == b1) atomicAdd(&sh.h2[(k >> 10) & 1023], 1u);
+        }
+    } else {
+        for (int64_t sb = 0; sb < rows; sb += kSelTile) {
+            const int64_t rb = sb + kSelPer * tid;
+            float v[kSelPer];
+            load_scores<kSelPer>(s, rb, rows, vec, v);
+#pragma unroll
+            for (int i = 0; i < kSelPer; i++) {
+                const uint32_t k = order_key(v[i]);
+                if (rb + i < rows && (k >> 20) == b1) atomicAdd(&sh.h2[(k >> 10) & 1023], 1u);
+            }
+        }
+    }
+    __syncthreads();
+
+    // second digit
+    const uint32_t need2 = keep - above1;
+    uint32_t c2[1] = {sh.h2[1023 - tid]};
+    uint32_t above2;
+    const uint32_t b2 = sel_find<1>(c2, need2, sh.tot[par++ & 1], sh.res, above2);
+    const uint32_t pre2 = (b1 << 10) | b2;
+    const uint32_t need3 = need2 - above2;
+    // third digit
+    if (in_lds) {
+        for (uint32_t i = tid; i < n_cand; i += kSelThreads) {
+            const uint32_t k = sh.key[i];
+            if ((k >> 10) == pre2) atomicAdd(&sh.h3[k & 1023], 1u);
+        }
+    } else {
+        for (int64_t sb = 0; sb < rows; sb += kSelTile) {
+            const int64_t rb = sb + kSelPer * tid;
+            float v[kSelPer];
+            load_scores<kSelPer>(s, rb, rows, vec, v);
+#pragma unroll
+            for (int i = 0; i < kSelPer; i++) {
+                const uint32_t k = order_key(v[i]);
+                if (rb + i < rows && (k >> 10) == pre2) atomicAdd(&sh.h3[k & 1023], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t c3[1] = {sh.h3[1023 - tid]};
+    uint32_t above3;
+    const uint32_t b3 = sel_find<1>(c3, need3, sh.tot[par++ & 1], sh.res, above3);
+    const uint32_t thr = (pre2 << 10) | b3;
+    const uint32_t m_eq = need3 - above3;          // rows equal to thr kept, lowest rows first
+
+    auto put = [&](uint32_t pos, int32_t r) {
+        if (pos >= keep) return;                    // never past the kept rows
+        if (kp == 1) {
+            dst[pos] = r;
+        } else {
+            for (int j = 0; j < kp; j++) dst[(size_t)pos * kp + j] = r * kp + j;
+        }
+    };
+    if (in_lds) {
+        // thread t takes candidates [per t, per (t + 1)), in row order
+        constexpr int kG = kSelCap / kSelThreads;
+        const uint32_t per = (n_cand + kSelThreads - 1) / kSelThreads;
+        const uint32_t i0 = per * tid;
+        uint32_t kk[kG];
+        int32_t rr[kG];
         uint32_t n_eq = 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const bool ok = rb + i < r1;
-            const uint32_t key = order_key(sv[i]);
-            gt[i] = ok && key > thr;
-            eq[i] = ok && key == thr;
-            n_eq += eq[i];
+        for (int u = 0; u < kG; u++) {
+            const uint32_t i = i0 + u;
+            const bool ok = u < (int)per && i < n_cand;
+            kk[u] = ok ? sh.key[i] : 0u;
+            rr[u] = ok ? sh.row[i] : -1;
+            if (!ok) kk[u] = 0u;
+            n_eq += (ok && kk[u] == thr) ? 1u : 0u;
         }
-        uint32_t tot_eq;
-        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, scan, tot_eq);
-        bool take[4];
-        uint32_t n_take = 0;
+        uint32_t tot;
+        const uint32_t eq0 = sel_scan(n_eq, sh.tot[par++ & 1], tot);
+        uint32_t take = 0, r = eq0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            take[i] = gt[i];
-            if (eq[i]) {
-                take[i] = eq_rank < info.eq_take;
-                eq_rank++;
-            }
-            n_take += take[i];
+        for (int u = 0; u < kG; u++) {
+            const bool ok = rr[u] >= 0;
+            const bool eq = ok && kk[u] == thr;
+            if (ok && (kk[u] > thr || (eq && r < m_eq))) take |= 1u << u;
+            r += eq ? 1u : 0u;
         }
-        uint32_t tot_take;
-        uint32_t pos = out_base + block_excl_scan(n_take, scan, tot_take);
+        uint32_t pos = sel_scan(__builtin_popcount(take), sh.tot[par++ & 1], tot);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            if (!take[i]) continue;
-            if (pos >= keep) break;                 // never past the kept rows
-            const int32_t r = (int32_t)(rb + i);
-            if (kp == 1) {
-                dst[pos] = r;
-            } else {
-                for (int j = 0; j < kp; j++) dst[(size_t)pos * kp + j] = r * kp + j;
+        for (int u = 0; u < kG; u++)
+            if ((take >> u) & 1) put(pos++, rr[u]);
+    } else {
+        uint32_t eq_done = 0, out_done = 0;
+        for (int64_t sb = 0; sb < rows; sb += kSelTile) {
+            const int64_t rb = sb + kSelPer * tid;
+            float v[kSelPer];
+            load_scores<kSelPer>(s, rb, rows, vec, v);
+            uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+            for (int i = 0; i < kSelPer; i++) {
+                const uint32_t k = order_key(v[i]);
+                if (rb + i < rows) {
+                    gtm |= (k > thr ? 1u : 0u) << i;
+                    eqm |= (k == thr ? 1u : 0u) << i;
+                }
             }
-            pos++;
+            uint32_t tot;
+            uint32_t r = eq_done + sel_scan(__builtin_popcount(eqm), sh.tot[par++ & 1], tot);
+            eq_done += tot;
+            uint32_t take = gtm;
+#pragma unroll
+            for (int i = 0; i < kSelPer; i++) {
+                if ((eqm >> i) & 1) {
+                    if (r < m_eq) take |= 1u << i;
+                    r++;
+                }
+            }
+            uint32_t pos = out_done + sel_scan(__builtin_popcount(take), sh.tot[par++ & 1], tot);
+            out_done += tot;
+#pragma unroll
+            for (int i = 0; i < kSelPer; i++)
+                if ((take >> i) & 1) put(pos++, (int32_t)(rb + i));
         }
-        eq_base += tot_eq;
-        out_base += tot_take;
     }
-    if (c == 0) {
-        const int32_t pooled = a.keep * kp;
-        const int32_t tail = qi.nvis - qi.rows * kp;
-        const int32_t cnt = pooled + tail;
-        for (int i = threadIdx.x; i < a.sel_ld - pooled; i += 256)
-            dst[pooled + i] = i < tail ? qi.rows * kp + i : -1;
-        if (threadIdx.x == 0) a.sel_count[q] = cnt;
-    }
+    // the unpooled tail, then padding
+    const int32_t pooled = a.keep * kp;
+    const int32_t tail = qi.nvis - (int32_t)rows * kp;
+    for (int i = tid; i < a.sel_ld - pooled; i += kSelThreads) dst[pooled + i] = i < tail ? (int32_t)rows * kp + i : -1;
+    if (tid == 0) a.sel_count[q] = pooled + tail;
 }
-
-// Zeroes a query's first-digit histogram (after a standalone
-// top-k; the fused step does this in the attention kernel).  grid (n_q).
-__device__ __forceinline__ void clear_topk_state(const Args &a, int q) {
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) a.hist[(size_t)q * kHistBins + i] = 0;
-}
-
-__global__ __launch_bounds__(256) void k_topk_clear(Args a) { clear_topk_state(a, blockIdx.x); }
 
 // ---------------------------------------------------------------- attention
 // One work-group = (query q, split sp), all 64 heads, 512 threads = 8 waves.
@@ -842,6 +895,27 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Reductions over lanes l and l ^ 16 (l ^ 32) with v_permlane16_swap
+// (v_permlane32_swap): with both operands x, the pair returned holds x at l
+// and at the partner lane.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float xor16_max(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // LDS-only work-group barrier: global accesses in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -856,7 +930,6 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
     __shared__ int32_t sidx[kMaxSplitRows];
     __shared__ f32x4 sx[8][2][64];                 // partial scores per wave
     const int q = blockIdx.y, sp = blockIdx.x;
-    if (a.clear_topk && sp == 0) clear_topk_state(a, q);
     const QInfo qi = query_info(a, q);
     const int lane = lane_id(), g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -903,35 +976,38 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
     }
     __syncthreads();
 
-    // DMA of step c's rows into buffer slot b: V parts of rows w, w+8,
-    // w+16, w+24; waves 0..3 also the RoPE tails of rows 8w..8w+7
+    // DMA of a step's rows into buffer slot b: V parts of rows w, w+8,
+    // w+16, w+24; waves 0..3 also the RoPE tails of rows 8w..8w+7.  iv holds
+    // the step's row index of lane & 31, ir that of row 8w + lane / 8.
     const bool rope_wave = D > 512 && w < 4;
-    auto issue = [&](int c, int b) {
+    auto issue = [&](int32_t iv, int32_t ir, int b) {
         uint8_t *vb = lds + b * Cfg::BUF;
-        const int32_t *si = sidx + kAttnRows * c;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int r = w + 8 * i;
-            const int32_t t = si[r];
+            const int32_t t = __builtin_amdgcn_readlane(iv, r);
             const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
             dma16(src + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(vb + r * Cfg::VS)));
         }
         if (rope_wave) {
             const int row = 8 * w + (lane >> 3);
-            const int32_t t = si[row];
-            const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
+            const uint8_t *src = ir >= 0 ? C + (size_t)ir * (2 * D) : kZeroRow;
             const int piece = (lane & 7) ^ (row & 7);
             dma16(src + 1024 + 16 * piece, __builtin_amdgcn_readfirstlane(lds_addr(vb + Cfg::VBYTES + 8 * w * 128)));
         }
     };
+    // row indices of step c (-1 past the split)
+    auto idx_v = [&](int c) -> int32_t { return c < nst ? sidx[kAttnRows * c + (lane & 31)] : -1; };
+    auto idx_r = [&](int c) -> int32_t { return c < nst ? sidx[kAttnRows * c + 8 * (w & 3) + (lane >> 3)] : -1; };
 
     f32x4 acc[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, l_part = 0.f;
 
-    if (nst > 0) issue(0, 0);
-    if (nst > 1) issue(1, 1);
+    int32_t iv_cur = idx_v(0), iv_n1 = idx_v(1), iv_n2 = idx_v(2), ir_n2 = idx_r(2);
+    if (nst > 0) issue(iv_cur, idx_r(0), 0);
+    if (nst > 1) issue(iv_n1, idx_r(1), 1);
     int b_cur = 0;
     for (int c = 0; c < nst; c++) {
         // this wave's DMA of step c is done (step c + 1's may be in flight),
@@ -945,10 +1021,15 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
             wait_vm<0>();
         }
         lds_barrier();
-        if (c + 2 < nst) issue(c + 2, b_cur == 0 ? 2 : b_cur - 1);
+        if (c + 2 < nst) issue(iv_n2, ir_n2, b_cur == 0 ? 2 : b_cur - 1);
         const uint8_t *vb = lds + b_cur * Cfg::BUF;
         b_cur = b_cur == 2 ? 0 : b_cur + 1;
-        const uint64_t okmask = __ballot(lane < kAttnRows && sidx[kAttnRows * c + (lane & 31)] >= 0);
+        const uint64_t okmask = __ballot(lane < kAttnRows && iv_cur >= 0);
+        // indices two steps ahead, read while this step computes
+        iv_cur = iv_n1;
+        iv_n1 = iv_n2;
+        iv_n2 = idx_v(c + 3);
+        ir_n2 = idx_r(c + 3);
 
         // partial S^T over this wave's half of the dimensions
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -998,8 +1079,8 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
             z[j] = v;
             cmax = fmaxf(cmax, v);
         }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        cmax = xor16_max(cmax);
+        cmax = xor32_max(cmax);
         const bool need = cmax > m_ref + 8.f;
         if (__any(need)) {
             const float m_new = need ? cmax : m_ref;
@@ -1045,8 +1126,7 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
         }
     }
     // total softmax mass per head over the four lane groups
-    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = xor32_sum(xor16_sum(l_part));
 
     const int col0 = 256 * x + 4 * g;
     if (a.n_split == 1) {
@@ -1159,18 +1239,8 @@ hipError_t launch_filter(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_resolve(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_resolve, dim3(a.n_q), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_clear(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk_clear, dim3(a.n_q), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_emit(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_emit, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+hipError_t launch_select(const Args &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_select, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ constexpr int kIdxHeads = 32;     // indexer heads
 constexpr int kIdxDim = 128;      // indexer head width
 constexpr int kHistBins = 4096;   // first radix digit: order-key bits 31..20
 constexpr int kMaxTopK = 4096;
-constexpr int kMaxChunks = 1024;  // top-k chunks per query (LDS arrays of k_emit)
+constexpr int kMaxChunks = 1024;  // top-k chunks per query (one per k_select thread)
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
 constexpr int kMaxSplitRows = 4096;  // selected rows per attention work-group
 
@@ -40,14 +40,6 @@ struct Plan {
     size_t off_pacc, off_pml, total;
 };
 
-// Per-(query, chunk) bookkeeping of the selection.
-struct ChunkInfo {
-    uint32_t gt;       // rows whose first digit exceeds the threshold bucket
-    uint32_t n_cand;   // rows in the threshold bucket (may exceed the slots)
-    uint32_t off;      // output position of the chunk's first selected row
-    uint32_t eq_take;  // rows equal to the threshold that this chunk keeps
-};
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q, int64_t max_nvis) {
@@ -71,7 +63,7 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     while ((p.max_rows + ch - 1) / ch > kMaxChunks) ch <<= 1;
     p.chunk = (int32_t)ch;
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
-    p.cand_cap = p.chunk / 4;     // a chunk's bucket rows beyond this take the slow path
+    p.cand_cap = p.chunk / 4;     // a chunk's candidates beyond this are found again by k_select
 
     // attention splits: aim at ~128 (query, split) work-groups (one CU
     // each), whole 32-row steps, 64..kMaxSplitRows rows per split; the
@@ -91,8 +83,8 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     size_t o = 0;
     p.off_hist = o;   o += align256((size_t)n_q * kHistBins * 4);
     p.ctrl_bytes = o;
-    p.off_thr = o;    o += align256((size_t)n_q * 4);
-    p.off_chunk = o;  o += align256((size_t)n_q * p.n_chunks * sizeof(ChunkInfo));
+    p.off_thr = o;    o += align256((size_t)n_q * 8);
+    p.off_chunk = o;  o += align256((size_t)n_q * p.n_chunks * 4);
     p.off_cand = o;   o += align256((size_t)n_q * p.n_chunks * p.cand_cap * 8);
     p.off_scores = o; o += align256((size_t)n_q * p.score_ld * 4);
     p.off_sel = o;    o += align256((size_t)n_q * p.sel_max * 4);

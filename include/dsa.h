@@ -178,7 +178,7 @@ int dsa_decode_step(const dsa_geometry *geom, const dsa_batch *batch,
  * dsa_decode_step call on this thread records events[0] on its stream before
  * its first kernel and events[i + 1] after its i-th kernel (as many as fit),
  * so elapsed(events[i], events[i + 1]) brackets kernel i.  Kernel order:
- * score, filter, resolve, emit, attend, split merge (seven events in all; the merge
+ * score, filter, select, attend, split merge (six events in all; the merge
  * interval is empty when the attention is not split).  Pass NULL/0 to stop.
  * Returns DSA_OK. */
 int dsa_set_timing_events(hipEvent_t *events, int32_t n_events);
