@@ -27,6 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_m128k_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "deepseek_sparse_attention_amd", "csrc", "dsa_kernels.hip")
 METRIC = "DSA decode queries/sec at 128K ctx, top-k 2048; achieved HBM GB/s vs peak"
 KERNELS = ["score", "filter", "select", "attend", "merge"]
 
@@ -47,6 +50,37 @@ def algorithmic_bytes(w):
     step = int(keys.sum()) + w.n_q * qi_w + sel_rows + q + out
     score_launch = int(keys.sum()) + w.n_q * qi_w
     return step, score_launch
+
+
+def score_kernel_hash() -> str:
+    """sha256 (16 hex digits) of the decode score kernel's source text, from
+    its template line to its closing brace."""
+    import hashlib
+    src = open(KERNEL_SRC).read()
+    i = src.index("template <bool STRIDE>\n__global__ __launch_bounds__(256) void k_score(Args a) {")
+    j = src.index("\n}\n", i) + 3
+    return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
+
+
+def measured_traffic(w):
+    """HBM bytes per k_score launch from the committed rocprofv3 counter
+    readings (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or
+    None if they were taken on another workload or another kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != w.name or t.get("kernel_sha") != score_kernel_hash():
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024))
+
+
+def prefill_score_flops(w) -> int:
+    """MFMA flops of the prefill scorer: 2 x 32 heads x 128 per scored row."""
+    g = w.geom
+    rows = w.q_nvis.astype("int64") // g["kpool"]
+    scored = rows[rows > g["top_k"] // g["kpool"]]
+    return int(2 * g["n_idx_heads"] * g["d_idx"] * scored.sum())
 
 
 def cpu_baseline(w, budget_s: float):
@@ -72,6 +106,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="m128k")
+    ap.add_argument("--batch", type=int, default=8, help="sequences at the 128K decode point (m128k only)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=6.0)
@@ -91,7 +126,10 @@ def main() -> int:
     torch.cuda.set_device(0)
     B.device_check()
     t0 = time.perf_counter()
-    w = I.config(args.config, poison_beyond=False)
+    if args.config == "m128k":
+        w = I.decode_128k(args.batch, poison_beyond=False)
+    else:
+        w = I.config(args.config, poison_beyond=False)
     print(f"[bench] {args.config}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
     reps = [DeviceWorkload(w) for _ in range(max(1, args.replicas))]
     R = len(reps)
@@ -137,7 +175,18 @@ def main() -> int:
         for j, k in enumerate(names):
             per[k] += row[j].elapsed_time(row[j + 1]) * 1e3 / n_rep
     score_us = per["score"]
-    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    prefill = w.n_seq == 1 and w.n_q > 1
+    if prefill:
+        flops = prefill_score_flops(w)
+        achieved = flops / (score_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": "k_score_prefill", "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": flops}
+    else:
+        achieved = score_bytes / (score_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_score", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w),
+                "bytes_per_launch": score_bytes}
 
     res = {
         "metric": METRIC,
@@ -157,9 +206,7 @@ def main() -> int:
         "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(v, 2) for k, v in per.items()},
-        "roofline": {"bound": "hbm", "kernel": "k_score", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": score_bytes},
+        "roofline": roof,
     }
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -178,9 +225,12 @@ def main() -> int:
 
 def _workload_name(w) -> str:
     g = w.geom
-    return (f"{w.name}: decode, {w.n_q} sequences x {int(w.q_nvis.max())} cached tokens, top-k {g['top_k']}, "
-            f"kpool {g['kpool']}, {g['n_heads']} heads x {g['d_latent'] + g['d_rope']} latent rows, "
-            f"indexer {g['n_idx_heads']}x{g['d_idx']}")
+    shape = (f"top-k {g['top_k']}, kpool {g['kpool']}, {g['n_heads']} heads x {g['d_latent'] + g['d_rope']} "
+             f"latent rows, indexer {g['n_idx_heads']}x{g['d_idx']}")
+    if w.n_seq == 1 and w.n_q > 1:
+        return (f"{w.name}: prefill chunk of {w.n_q} consecutive positions ending at {int(w.q_nvis.max())} "
+                f"cached tokens, {shape}")
+    return f"{w.name}: decode, {w.n_q} sequences x {int(w.q_nvis.max())} cached tokens, {shape}"
 
 
 if __name__ == "__main__":

@@ -208,8 +208,16 @@ def config(name: str, **kw) -> Workload:
         T = 1 << 20
         return make_workload("c4", 4, GEOM_KPOOL, 1, T, [0], [T - 1], **kw)
     if name == "m128k":  # decode metric point: B=8, T=131072, k=2048
-        return make_workload("m128k", 5, GEOM_TOKEN, 8, 131072, np.arange(8), [131072] * 8, **kw)
+        return decode_128k(8, **kw)
     raise KeyError(name)
+
+
+def decode_128k(batch: int, **kw) -> Workload:
+    """The 128K decode point with ``batch`` sequences (the metric point has
+    8); sequence s is drawn from its own streams, so the first 8 sequences
+    are the same at every batch size."""
+    name = "m128k" if batch == 8 else f"m128k_b{batch}"
+    return make_workload(name, 5, GEOM_TOKEN, batch, 131072, np.arange(batch), [131072] * batch, **kw)
 
 
 def c3_small(**kw) -> Workload:
