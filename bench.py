@@ -19,6 +19,8 @@ from __future__ import annotations
 
 import argparse
 import json
+
+import numpy as np
 import os
 import sys
 import time
@@ -40,7 +42,11 @@ def algorithmic_bytes(w):
     g = w.geom
     D = g["d_latent"] + g["d_rope"]
     rows = w.q_nvis.astype("int64") // g["kpool"]
-    keys = rows * g["d_idx"] * 2
+    # keys: each sequence's visible rows once, however many of its queries read them
+    seq_rows = {}
+    for s_, r in zip(w.q_seq.tolist(), rows.tolist()):
+        seq_rows[s_] = max(seq_rows.get(s_, 0), r)
+    keys = np.array(list(seq_rows.values()), dtype=np.int64) * g["d_idx"] * 2
     qi_w = g["n_idx_heads"] * g["d_idx"] * 2 + g["n_idx_heads"] * 4
     kp, keep = g["kpool"], g["top_k"] // g["kpool"]
     kept = [int(n) if int(n) // kp <= keep else keep * kp + int(n) % kp for n in w.q_nvis]
@@ -107,6 +113,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="m128k")
     ap.add_argument("--batch", type=int, default=8, help="sequences at the 128K decode point (m128k only)")
+    ap.add_argument("--window", type=int, default=1,
+                    help="query rows per sequence at the last positions (speculative verify; m128k only)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=6.0)
@@ -126,7 +134,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     B.device_check()
     t0 = time.perf_counter()
-    if args.config == "m128k":
+    if args.config == "m128k" and args.window > 1:
+        w = I.decode_window(args.batch, args.window, poison_beyond=False)
+    elif args.config == "m128k":
         w = I.decode_128k(args.batch, poison_beyond=False)
     else:
         w = I.config(args.config, poison_beyond=False)
@@ -230,6 +240,9 @@ def _workload_name(w) -> str:
     if w.n_seq == 1 and w.n_q > 1:
         return (f"{w.name}: prefill chunk of {w.n_q} consecutive positions ending at {int(w.q_nvis.max())} "
                 f"cached tokens, {shape}")
+    if w.n_q > w.n_seq:
+        return (f"{w.name}: verify windows, {w.n_seq} sequences x {w.n_q // w.n_seq} rows at the last positions "
+                f"of {int(w.q_nvis.max())} cached tokens, {shape}")
     return f"{w.name}: decode, {w.n_q} sequences x {int(w.q_nvis.max())} cached tokens, {shape}"
 
 

@@ -126,7 +126,8 @@ dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &
     a.split_rows = p.split_rows;
     a.n_split = p.n_split;
     a.score_tile = p.score_tile;
-    a.prefill = b->q_per_seq_hint >= 8 ? 1 : 0;
+    a.prefill = b->q_per_seq_hint >= 2 ? 1 : 0;
+    a.pf_run = b->q_per_seq_hint;
     return a;
 }
 

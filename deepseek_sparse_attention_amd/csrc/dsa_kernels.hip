@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <functional>
+#include <type_traits>
 
 #include "dsa_args.h"
 
@@ -52,7 +53,6 @@ __device__ __forceinline__ uint32_t order_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kPfQ = 8;          // queries per prefill work-group
 
 struct QInfo {
     int32_t seq, nvis, rows, mode;   // mode 0 dense, 1 sparse, 2 invalid
@@ -72,7 +72,28 @@ __device__ __forceinline__ QInfo query_info(const Args &a, int q) {
     return r;
 }
 
+constexpr int kPfQ = 8;          // queries per prefill work-group
+
 __device__ __forceinline__ int query_seq(const Args &a, int q) { return a.q_seq ? a.q_seq[q] : q; }
+
+// Prefill blocks: every run of pf_run consecutive queries is covered by
+// ceil(pf_run / kPfQ) blocks of up to kPfQ of its queries.  Block blk
+// covers queries [first, last); pf_leader(q) is the first query of q's block.
+__device__ __forceinline__ int pf_blocks_per_run(const Args &a) { return (a.pf_run + kPfQ - 1) / kPfQ; }
+__device__ __forceinline__ int pf_block(const Args &a, int blk, int &last) {
+    const int per = pf_blocks_per_run(a);
+    const int run = blk / per, j = blk - run * per;
+    const int first = run * a.pf_run + j * kPfQ;
+    int e = first + kPfQ;
+    const int run_end = (run + 1) * a.pf_run;
+    e = e < run_end ? e : run_end;
+    last = e < a.n_q ? e : a.n_q;
+    return first;
+}
+__device__ __forceinline__ int pf_leader(const Args &a, int q) {
+    const int run = q / a.pf_run, off = q - run * a.pf_run;
+    return run * a.pf_run + (off / kPfQ) * kPfQ;
+}
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
@@ -153,6 +174,27 @@ __device__ uint32_t find_bucket(const uint32_t *hist, uint32_t need, uint32_t *s
     return b;
 }
 
+// Reductions over lanes l and l ^ 16 (l ^ 32) with v_permlane16_swap
+// (v_permlane32_swap): with both operands x, the pair returned holds x at l
+// and at the partner lane.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float xor16_max(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ---------------------------------------------------------------- workspace
 __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
     size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -181,7 +223,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     const QInfo qi = query_info(a, q);
     if (qi.mode == 2) return;
     if (a.fused && qi.mode == 0) return;
-    if (a.prefill && qi.seq == query_seq(a, q - q % kPfQ)) return;   // done by k_score_prefill
+    if (a.prefill && qi.seq == query_seq(a, pf_leader(a, q))) return;   // done by k_score_prefill
     const int64_t rows = qi.rows;
     if ((int64_t)blockIdx.x * a.score_tile >= rows) return;
     const bool hist = a.fused != 0;
@@ -274,16 +316,19 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     }
 }
 
-// Chunked-prefill indexer: a dense [8 queries x 32 heads] x [128 x keys]
-// contraction per work-group.  grid (key ranges, query blocks of 8), 512
-// threads = 8 waves, wave w computes query 8*blockIdx.y + w.  The block's
-// queries are consecutive positions of one sequence (the leader's); a
+// Chunked-prefill / verify-window indexer: a dense [queries x 32 heads] x
+// [128 x keys] contraction per work-group.  grid (key ranges, blocks), 512
+// threads = 8 waves.  A block holds up to 8 consecutive queries of one run
+// (pf_block); they are positions of one sequence (the leader's), and a
 // query of another sequence is left to the fix-up pass of k_score.  Key
-// tiles of 128 rows are loaded with coalesced 16-byte loads (512 threads
-// x 4 = 32 KiB), staged swizzled in LDS (double buffer) and shared by the
-// eight queries; causality masks the scores and the histogram per query
-// (a query scores rows < rows(q)).  Per-query first-digit histograms live
-// in LDS as 16-bit counters, two to a word.
+// tiles of 128 rows are loaded with coalesced 16-byte loads (512 threads x
+// 4 = 32 KiB), staged swizzled in LDS (double buffer) and shared by the
+// block's queries.  With P = the block's query count rounded up to a power
+// of two, wave w computes query w * P / 8 on 16-row blocks [NB s, NB s + NB)
+// of each tile, NB = P and s = w % (8 / P): every wave has work however few
+// queries the block holds.  Causality masks the scores and the histogram
+// per query (a query scores rows < rows(q)).  Per-query first-digit
+// histograms live in LDS as 16-bit counters, two to a word.
 constexpr int kPfTile = 128;     // key rows per LDS tile
 constexpr int kPfRange = 4096;   // key rows per work-group
 
@@ -292,19 +337,26 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     __shared__ uint32_t lh[kPfQ][kHistBins / 2];
     __shared__ int32_t sh_rows[kPfQ];
     const int w = threadIdx.x >> 6, lane = lane_id(), g = lane >> 4, n = lane & 15;
-    const int q0 = blockIdx.y * kPfQ;
-    const int q = q0 + w;
+    int q_end;
+    const int q0 = pf_block(a, blockIdx.y, q_end);
+    if (q0 >= q_end) return;                 // past the last query
+    const int nq = q_end - q0;
+    const int P = nq > 4 ? 8 : (nq > 2 ? 4 : nq);
+    const int slot = w * P / kPfQ;           // this wave's query within the block
+    const int sl = w % (kPfQ / P);           // and its share of each tile
+    const int q = q0 + slot;
     const int lead = query_seq(a, q0);
     const bool hist = a.fused != 0;
-    // does this wave's query take part, and up to which row
-    if (lane == 0) {
+    // does each query slot take part, and up to which row
+    if (threadIdx.x < kPfQ) {
         int32_t rr = 0;
-        if (q < a.n_q) {
-            const QInfo qi = query_info(a, q);
+        const int qs = q0 + (int)threadIdx.x;
+        if (qs < q_end) {
+            const QInfo qi = query_info(a, qs);
             const bool part = qi.mode != 2 && !(a.fused && qi.mode == 0) && qi.seq == lead;
             rr = part ? qi.rows : 0;
         }
-        sh_rows[w] = rr;
+        sh_rows[threadIdx.x] = rr;
     }
     __syncthreads();
     int32_t kmax = 0;
@@ -313,26 +365,26 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     const int64_t k0 = (int64_t)blockIdx.x * kPfRange;
     if (k0 >= kmax) return;
     const int64_t k1 = k0 + kPfRange < kmax ? k0 + kPfRange : kmax;
-    const int32_t my_rows = sh_rows[w];
+    const int32_t my_rows = sh_rows[slot];
     if (hist)
         for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) (&lh[0][0])[i] = 0;
 
     bf16x8 qa[2][4];
     float wt[2][4];
+    const int qv = slot < nq ? q : q0;       // a valid query for the idle slots (no rows)
     {
-        const int qq = q < a.n_q ? q : q0;
-        const uint16_t *qip = a.idx_q + (size_t)qq * kIdxHeads * kIdxDim;
+        const uint16_t *qip = a.idx_q + (size_t)qv * kIdxHeads * kIdxDim;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++) {
 #pragma unroll
             for (int s = 0; s < 4; s++)
                 qa[mb][s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qip + (16 * mb + n) * kIdxDim + 32 * s + 8 * g));
 #pragma unroll
-            for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)qq * kIdxHeads + 16 * mb + 4 * g + r];
+            for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)qv * kIdxHeads + 16 * mb + 4 * g + r];
         }
     }
     const uint8_t *K = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)lead * a.key_stride * kIdxDim);
-    float *srow = a.scores + (size_t)(q < a.n_q ? q : 0) * a.score_ld;
+    float *srow = a.scores + (size_t)qv * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
 
     u32x4 v[4];
@@ -353,56 +405,87 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
             *(u32x4 *)(&ktile[buf][r * 256 + 16 * (pc ^ (r & 7))]) = v[i];
         }
     };
-    fetch(k0);
-    int buf = 0;
-    for (int64_t base = k0; base < k1; base += kPfTile, buf ^= 1) {
-        stage(buf);
-        if (base + kPfTile < k1) fetch(base + kPfTile);
-        __syncthreads();
-        const uint8_t *tb = ktile[buf];
+    // partial score of 16-row block rb of the tile: lane (g, n) holds row n's
+    // heads 4g..4g+3 and 16+4g..16+4g+3, weighted and rectified
+    auto block_part = [&](const uint8_t *tb, int rb) -> float {
+        const int r = 16 * rb + n;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 2; j++) {                    // two groups of 64 keys
-            float p[4];
+        for (int s = 0; s < 4; s++) {
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], bv, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], bv, acc1, 0, 0, 0);
+        }
+        float x = 0.f;
 #pragma unroll
-            for (int st = 0; st < 4; st++) {
-                const int r = 64 * j + 16 * st + n;
-                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], bv, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], bv, acc1, 0, 0, 0);
-                }
-                float x = 0.f;
-#pragma unroll
-                for (int rr = 0; rr < 4; rr++) {
-                    x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
-                    x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
-                }
-                p[st] = x;
-            }
-            const bool b0 = g & 1, b1 = (g >> 1) & 1;
-            const float send0 = b0 ? p[0] : p[2], send1 = b0 ? p[1] : p[3];
-            const float keep0 = b0 ? p[2] : p[0], keep1 = b0 ? p[3] : p[1];
-            const float q0s = keep0 + __shfl_xor(send0, 16, 64);
-            const float q1s = keep1 + __shfl_xor(send1, 16, 64);
-            const float score = (b1 ? q1s : q0s) + __shfl_xor(b1 ? q0s : q1s, 32, 64);
-            const int64_t row = base + 64 * j + 16 * st_mine + n;
-            if (row < my_rows) {
-                srow[row] = score;
-                if (hist) {
-                    const uint32_t bin = order_key(score) >> 20;
-                    atomicAdd(&lh[w][bin >> 1], 1u << (16 * (bin & 1)));
-                }
+        for (int rr = 0; rr < 4; rr++) {
+            x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
+            x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
+        }
+        return x;
+    };
+    auto emit = [&](int64_t row, float score) {
+        if (row < my_rows) {
+            srow[row] = score;
+            if (hist) {
+                const uint32_t bin = order_key(score) >> 20;
+                atomicAdd(&lh[slot][bin >> 1], 1u << (16 * (bin & 1)));
             }
         }
-        __syncthreads();                                  // buffer free for the tile after next
-    }
+    };
+    auto tiles = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        fetch(k0);
+        int buf = 0;
+        for (int64_t base = k0; base < k1; base += kPfTile, buf ^= 1) {
+            stage(buf);
+            if (base + kPfTile < k1) fetch(base + kPfTile);
+            __syncthreads();
+            const uint8_t *tb = ktile[buf];
+            if (NB >= 4) {
+                // groups of four blocks: the four lane groups end up holding
+                // one block's full score each
+#pragma unroll
+                for (int j = 0; j < NB / 4; j++) {
+                    const int rb0 = NB * sl + 4 * j;
+                    float p[4];
+#pragma unroll
+                    for (int st = 0; st < 4; st++) p[st] = block_part(tb, rb0 + st);
+                    const bool b0 = g & 1, b1 = (g >> 1) & 1;
+                    const float send0 = b0 ? p[0] : p[2], send1 = b0 ? p[1] : p[3];
+                    const float keep0 = b0 ? p[2] : p[0], keep1 = b0 ? p[3] : p[1];
+                    const float q0s = keep0 + __shfl_xor(send0, 16, 64);
+                    const float q1s = keep1 + __shfl_xor(send1, 16, 64);
+                    const float score = (b1 ? q1s : q0s) + __shfl_xor(b1 ? q0s : q1s, 32, 64);
+                    emit(base + 16 * (rb0 + st_mine) + n, score);
+                }
+            } else {
+                // one or two blocks: full sum over the lane groups, written
+                // by lane group 0
+#pragma unroll
+                for (int j = 0; j < NB; j++) {
+                    const int rb = NB * sl + j;
+                    const float score = xor32_sum(xor16_sum(block_part(tb, rb)));
+                    if (g == 0) emit(base + 16 * rb + n, score);
+                }
+            }
+            __syncthreads();                              // buffer free for the tile after next
+        }
+    };
+    if (P == 8)
+        tiles(std::integral_constant<int, 8>());
+    else if (P == 4)
+        tiles(std::integral_constant<int, 4>());
+    else if (P == 2)
+        tiles(std::integral_constant<int, 2>());
+    else
+        tiles(std::integral_constant<int, 1>());
     if (hist) {
+        __syncthreads();
         for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) {
             const int qq = q0 + i / (kHistBins / 2);
             const uint32_t word = (&lh[0][0])[i];
-            if (!word || qq >= a.n_q) continue;
+            if (!word || qq >= q_end) continue;
             const int bin = 2 * (i % (kHistBins / 2));
             uint32_t *gh = a.hist + (size_t)qq * kHistBins + bin;
             if (word & 0xFFFFu) atomicAdd(gh, word & 0xFFFFu);
@@ -895,27 +978,6 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Reductions over lanes l and l ^ 16 (l ^ 32) with v_permlane16_swap
-// (v_permlane32_swap): with both operands x, the pair returned holds x at l
-// and at the partner lane.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float xor16_max(float x) {
-    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-    const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
 // LDS-only work-group barrier: global accesses in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -1215,7 +1277,9 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
 hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
     if (a.prefill) {
         const unsigned ranges = (unsigned)((max_rows + kPfRange - 1) / kPfRange);
-        hipLaunchKernelGGL(k_score_prefill, dim3(ranges, (a.n_q + kPfQ - 1) / kPfQ), dim3(512), 0, st, a);
+        const unsigned runs = (unsigned)((a.n_q + a.pf_run - 1) / a.pf_run);
+        const unsigned per = (unsigned)((a.pf_run + kPfQ - 1) / kPfQ);
+        hipLaunchKernelGGL(k_score_prefill, dim3(ranges, runs * per), dim3(512), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -220,6 +220,15 @@ def decode_128k(batch: int, **kw) -> Workload:
     return make_workload(name, 5, GEOM_TOKEN, batch, 131072, np.arange(batch), [131072] * batch, **kw)
 
 
+def decode_window(batch: int, window: int, T: int = 131072, **kw) -> Workload:
+    """Speculative verify: ``batch`` sequences of T cached tokens, each with a
+    window of ``window`` query rows at the last positions (row i sees
+    T - window + 1 + i tokens), consecutive per sequence."""
+    q_seq = np.repeat(np.arange(batch), window)
+    q_nvis = np.tile(T - window + 1 + np.arange(window), batch)
+    return make_workload(f"win{window}_b{batch}", 6, GEOM_TOKEN, batch, T, q_seq, q_nvis, **kw)
+
+
 def c3_small(**kw) -> Workload:
     """Prefill variant whose chunk sits at positions 0..511 of a 4096-token
     context, so that early queries keep fewer than top-k candidates."""

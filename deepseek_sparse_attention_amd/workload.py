@@ -3,10 +3,22 @@ step on it.  Plumbing only: torch allocates and uploads, the C ABI computes.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import binding as B
 from .inputs import Workload
+
+
+def run_hint(q_seq) -> int:
+    """Length of the runs of consecutive queries that share a sequence, if
+    every run has the same length >= 2, else 0 (no hint)."""
+    q_seq = np.asarray(q_seq)
+    if q_seq.size < 2:
+        return 0
+    cut = np.flatnonzero(np.diff(q_seq) != 0) + 1
+    lengths = np.diff(np.concatenate(([0], cut, [q_seq.size])))
+    return int(lengths[0]) if lengths[0] >= 2 and (lengths == lengths[0]).all() else 0
 
 
 class DeviceWorkload:
@@ -36,8 +48,7 @@ class DeviceWorkload:
                                device=dev)
         self.lse = torch.empty((self.n_q, self.geom["n_heads"]), dtype=torch.float32, device=dev)
         self.ws = B.new_workspace(self.geom, self.n_q, self.max_nvis, device=dev)
-        hint = self.n_q if (w.n_seq == 1 and self.n_q > 1) else 0
-        self.batch = B.batch(self.q_seq, self.q_nvis, self.max_nvis, w.n_seq, hint)
+        self.batch = B.batch(self.q_seq, self.q_nvis, self.max_nvis, w.n_seq, run_hint(w.q_seq))
 
     def decode_step(self, stream=None, with_sel: bool = True) -> None:
         B.decode_step(self.geom, self.batch, self.idx_q, self.idx_w, self.idx_k, self.w.key_rows, self.q,

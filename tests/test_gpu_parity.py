@@ -291,3 +291,47 @@ def test_prefill_runs_with_mixed_sequences():
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, "prefill mixed")
     check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, "prefill mixed")
+
+
+@pytest.mark.parametrize("window", [2, 3, 5, 8, 9])
+def test_verify_window_matches_oracle(window):
+    """Speculative verify windows: B sequences x `window` rows at the last
+    positions; each run of rows shares its key tiles in the prefill scorer.
+    Scores bit-exact, selections bit-exact, attention within tolerance."""
+    log(f"verify window {window}")
+    w = I.decode_window(3, window, T=6000)
+    dw = DeviceWorkload(w)
+    assert dw.batch.q_per_seq_hint == window
+    ld = dw.max_nvis + 1
+    scores = torch.full((w.n_q, ld), float("nan"), device="cuda")
+    B.index_scores(w.geom, dw.batch, dw.idx_q, dw.idx_w, dw.idx_k, w.key_rows, scores, ld)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    ref = O.index_scores(w.q_seq, w.q_nvis, 1, w.idx_q, w.idx_w, w.idx_k, score_ld=ld)
+    got = scores.cpu().numpy()
+    for j in range(w.n_q):
+        rows = int(w.q_nvis[j])
+        assert np.array_equal(got[j, :rows], ref[j, :rows]), f"query {j}"
+        assert np.isnan(got[j, rows:]).all(), f"query {j} wrote past rows"
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, f"window {window}")
+    check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, f"window {window}")
+
+
+def test_run_hint_that_does_not_match_the_runs():
+    """A run-length hint that disagrees with the real runs (and a query count
+    that is not a multiple of it) still gives exact results: queries outside
+    their block leader's sequence go through the fix-up pass."""
+    log("mismatched run hint")
+    T = 4000
+    q_seq = [0, 0, 0, 1, 1, 1, 2, 2, 0, 1, 2]
+    nvis = [3990, 3991, 3992, 2500, 2501, 2502, 3999, 4000, 1000, 3500, 2049]
+    w = I.make_workload("hint", 16, I.GEOM_TOKEN, 3, T, q_seq, nvis)
+    dw = DeviceWorkload(w)
+    for hint in (4, 16):
+        dw.batch = B.batch(dw.q_seq, dw.q_nvis, dw.max_nvis, w.n_seq, hint)
+        dw.decode_step()
+        torch.cuda.synchronize()
+        sel, cnt, out, lse = oracle_decode(w)
+        check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, f"hint {hint}")
+        check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, f"hint {hint}")
