@@ -278,3 +278,88 @@ int oracle_decode_step(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
     free(scores);
     return rc;
 }
+
+/*
+ * k-pool key producer.
+ *
+ * [WA] "DeepSeek Sparse Attention, k-pool flavour": a pool's compressed key
+ * is one 128-wide vector per four adjacent tokens, computed once, when the
+ * pool's last token arrives; the per-step state is a rolling buffer of the
+ * (key, gate) pairs of the pool being filled plus an append-only array of
+ * finished pool keys.  [TS] "GLM-5.3-Flash (glm5next)" table: [key|gate] is
+ * cached per cell and a softmax over the gates, plus a per-slot position
+ * embedding, compresses each pool.
+ *
+ * Readings: the softmax runs over the four slots separately for every key
+ * dimension d ([ST]'s verification notes list "one softmax over the whole
+ * pool block instead of per key-dim" as a rival that must disagree), and the
+ * position embedding E[j][d] is added to the gate logit:
+ *     K[d] = sum_j exp(a_j) key_j[d] / sum_j exp(a_j),   a_j = gate_j[d] + E[j][d].
+ * A cell is key (d_idx bf16) followed by gate (d_idx bf16).  The pool key is
+ * stored as bf16, rounded to nearest (ties to even) from the double value.
+ */
+
+/* Nearest bf16 (ties to even) of a double in the normal range. */
+static uint16_t bf16_from_double(double v)
+{
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    int e;
+    const double m = frexp(fabs(v), &e);         /* |v| = m * 2^e, m in [0.5, 1) */
+    const double r = rint(ldexp(m, 8));          /* 8 significant bits, ties to even */
+    float f = (float)ldexp(r, e - 8);            /* exact */
+    if (v < 0) f = -f;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Compresses the four cells c[j] (each 2 * d_idx bf16) into out[d_idx]. */
+static void pool_compress(const uint16_t *const c[4], int32_t d_idx, const float *pos_emb, uint16_t *out)
+{
+    for (int32_t d = 0; d < d_idx; d++) {
+        double a[4], m = -INFINITY;
+        for (int j = 0; j < 4; j++) {
+            a[j] = bf16_value(c[j][d_idx + d]) + (double)pos_emb[j * d_idx + d];
+            if (a[j] > m) m = a[j];
+        }
+        double num = 0.0, den = 0.0;
+        for (int j = 0; j < 4; j++) {
+            const double e = exp(a[j] - m);
+            num += e * bf16_value(c[j][d]);
+            den += e;
+        }
+        out[d] = bf16_from_double(num / den);
+    }
+}
+
+/*
+ * Appends n_new[s] tokens to sequence s, which holds n_tok[s] tokens: token
+ * t = n_tok[s] + i takes its cell from new_kg[s][i] into rolling slot t mod 4;
+ * when that slot is 3, pool t / 4 is complete and its key is written to
+ * pool_keys[s][t / 4].  Token by token, in order.
+ *   new_kg    [n_seq][new_stride][2 d_idx]  bf16
+ *   rolling   [n_seq][4][2 d_idx]           bf16 (read and updated)
+ *   pool_keys [n_seq][pool_stride][d_idx]   bf16
+ *   pos_emb   [4][d_idx]                    float
+ */
+int oracle_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new,
+                       const uint16_t *new_kg, int64_t new_stride, int32_t d_idx,
+                       uint16_t *rolling, uint16_t *pool_keys, int64_t pool_stride,
+                       const float *pos_emb)
+{
+    const int64_t cell = 2 * (int64_t)d_idx;
+    for (int32_t s = 0; s < n_seq; s++) {
+        uint16_t *roll = rolling + (int64_t)s * 4 * cell;
+        for (int32_t i = 0; i < n_new[s]; i++) {
+            const int64_t t = (int64_t)n_tok[s] + i;
+            const int slot = (int)(t % 4);
+            memcpy(roll + slot * cell, new_kg + ((int64_t)s * new_stride + i) * cell,
+                   (size_t)cell * sizeof *roll);
+            if (slot == 3) {
+                const uint16_t *c[4] = {roll, roll + cell, roll + 2 * cell, roll + 3 * cell};
+                pool_compress(c, d_idx, pos_emb, pool_keys + ((int64_t)s * pool_stride + t / 4) * d_idx);
+            }
+        }
+    }
+    return 0;
+}

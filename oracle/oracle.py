@@ -39,6 +39,7 @@ def load(path: str):
     L.oracle_decode_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f32, i32, i32,
                                      P, P, P, i64, P, P, i64, P, i32, P, P, P]
     L.oracle_max_threads.argtypes = []
+    L.oracle_pool_append.argtypes = [i32, P, P, P, i64, i32, P, P, i64, P]
     for f in (L.oracle_index_scores, L.oracle_topk, L.oracle_mla_attend,
               L.oracle_decode_step, L.oracle_max_threads):
         f.restype = ctypes.c_int
@@ -138,3 +139,25 @@ def decode_step(geom, q_seq, q_nvis, idx_q, idx_w, idx_k, q, cache, sel_ld=None,
                                   _p(sel), sel_ld, _p(cnt), _p(out), _p(lse))
     assert rc == 0
     return sel, cnt, out, lse
+
+
+def pool_append(n_tok, n_new, new_kg, rolling, pool_keys, pos_emb, L=None):
+    """k-pool key producer, token by token.  Updates ``rolling`` and
+    ``pool_keys`` in place (uint16 bf16 bits) and returns them.
+
+    n_tok, n_new: int [n_seq]; new_kg: uint16 [n_seq, new_stride, 2 d_idx];
+    rolling: uint16 [n_seq, 4, 2 d_idx]; pool_keys: uint16 [n_seq, pool_stride, d_idx];
+    pos_emb: float32 [4, d_idx]."""
+    n_tok, n_new = _c(n_tok, np.int32), _c(n_new, np.int32)
+    new_kg, pos_emb = _c(new_kg, np.uint16), _c(pos_emb, np.float32)
+    assert rolling.dtype == np.uint16 and rolling.flags.c_contiguous
+    assert pool_keys.dtype == np.uint16 and pool_keys.flags.c_contiguous
+    n_seq, stride, cell = new_kg.shape
+    d_idx = cell // 2
+    assert rolling.shape == (n_seq, 4, cell) and pool_keys.shape[0] == n_seq and pool_keys.shape[2] == d_idx
+    assert pos_emb.shape == (4, d_idx) and (n_new <= stride).all()
+    assert ((n_tok + n_new) // 4 <= pool_keys.shape[1]).all()
+    rc = (L or lib()).oracle_pool_append(n_seq, _p(n_tok), _p(n_new), _p(new_kg), stride, d_idx,
+                                         _p(rolling), _p(pool_keys), pool_keys.shape[1], _p(pos_emb))
+    assert rc == 0
+    return rolling, pool_keys

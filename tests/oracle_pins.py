@@ -331,4 +331,120 @@ def pin_decode_is_composition(L):
         assert np.array_equal(o1[0], out[j]) and np.array_equal(s1[0], sel[j])
 
 
+# ---------------------------------------------------------------- pool keys
+def _pool_one(L, keys4, gates4, pos_emb):
+    """Key of one pool from four cells, through the oracle's append."""
+    kg = np.concatenate([bf(keys4), bf(gates4)], axis=-1)[None]        # [1, 4, 2 DI]
+    roll = np.zeros((1, 4, 2 * DI), np.uint16)
+    pk = np.zeros((1, 1, DI), np.uint16)
+    O.pool_append([0], [4], kg, roll, pk, np.asarray(pos_emb, np.float32), L=L)
+    return pk[0, 0]
+
+
+def pin_pool_equal_logits_give_mean(L):
+    """Logits equal over the four slots weight them equally, so the pool key
+    is the mean of the four keys (exact for integer keys: a multiple of 1/4)."""
+    rng = np.random.default_rng(31)
+    keys = rng.integers(-8, 9, size=(4, DI)).astype(np.float32)
+    gates = np.tile(rng.standard_normal(DI).astype(np.float32), (4, 1))
+    assert np.array_equal(fl(_pool_one(L, keys, gates, np.zeros((4, DI)))), keys.mean(0))
+    pos = np.tile(rng.standard_normal(DI).astype(np.float32), (4, 1))
+    assert np.array_equal(fl(_pool_one(L, keys, gates, pos)), keys.mean(0))
+
+
+def pin_pool_dominant_slot(L):
+    """A slot whose logit exceeds the others' by 800 takes all the weight
+    (exp(-800) underflows to 0), per key dimension: the pool key is that
+    slot's key, whether the margin comes from the gate or from the slot's
+    position embedding."""
+    rng = np.random.default_rng(32)
+    keys = rng.integers(-8, 9, size=(4, DI)).astype(np.float32)
+    dom = (np.arange(DI) * 7 + 3) % 4
+    want = keys[dom, np.arange(DI)]
+    gates = np.zeros((4, DI), np.float32)
+    gates[dom, np.arange(DI)] = 800.0
+    assert np.array_equal(fl(_pool_one(L, keys, gates, np.zeros((4, DI)))), want)
+    pos = np.zeros((4, DI), np.float32)
+    pos[dom, np.arange(DI)] = 800.0
+    assert np.array_equal(fl(_pool_one(L, keys, np.zeros((4, DI)), pos)), want)
+
+
+def pin_pool_constant_keys(L):
+    """Four equal keys give that key under any weights."""
+    rng = np.random.default_rng(33)
+    c = fl(bf(rng.standard_normal(DI)))
+    out = _pool_one(L, np.tile(c, (4, 1)), rng.standard_normal((4, DI)) * 3, rng.standard_normal((4, DI)))
+    assert np.array_equal(fl(out), c)
+
+
+def pin_pool_convex_and_shift_invariant(L):
+    """The pool key lies between the smallest and largest of the four keys in
+    every dimension, and adding one constant to every slot's logit of a
+    dimension changes nothing (softmax shift invariance)."""
+    rng = np.random.default_rng(34)
+    for _ in range(20):
+        keys = fl(bf(rng.standard_normal((4, DI)) * 4))
+        gates = rng.standard_normal((4, DI)) * 2
+        pos = np.round(rng.standard_normal((4, DI)) * 256) / 256       # exact in float32
+        out = fl(_pool_one(L, keys, gates, pos))
+        assert (out >= keys.min(0)).all() and (out <= keys.max(0)).all()
+        shift = np.tile(np.round(rng.standard_normal(DI)) * 2, (4, 1))  # even integers: sums stay exact
+        assert np.array_equal(fl(_pool_one(L, keys, gates, pos + shift)), out)
+
+
+def pin_pool_rounding(L):
+    """The stored key is the nearest bf16, ties to even: with equal logits,
+    keys (1+2^-7, 1+2^-7, 1+2^-7, 1) average 1 + 3*2^-9 -> 1+2^-7, and
+    (1+2^-7, 1+2^-7, 1, 1) average 1 + 2^-8, halfway -> 1 (even)."""
+    a, b = 1.0 + 2.0 ** -7, 1.0
+    g = np.zeros((4, DI))
+    z = np.zeros((4, DI))
+    up = _pool_one(L, np.array([[a], [a], [a], [b]]) * np.ones((4, DI)), g, z)
+    tie = _pool_one(L, np.array([[a], [a], [b], [b]]) * np.ones((4, DI)), g, z)
+    neg = _pool_one(L, -np.array([[a], [a], [a], [b]]) * np.ones((4, DI)), g, z)
+    assert (fl(up) == a).all() and (fl(tie) == b).all() and (fl(neg) == -a).all()
+
+
+def pin_pool_append_semantics(L):
+    """Appending tokens one by one, in chunks or all at once gives the same
+    pool keys and rolling buffer; pool p depends on cells 4p..4p+3 only; the
+    rolling buffer holds the cells of the pool being filled at slot t mod 4;
+    pools not yet complete are not written."""
+    rng = np.random.default_rng(35)
+    n = np.array([23, 14, 3], np.int32)
+    cells = np.concatenate([bf(rng.standard_normal((3, 23, DI)) * 3),
+                            bf(rng.standard_normal((3, 23, DI)))], axis=-1)
+    pos = rng.standard_normal((4, DI)).astype(np.float32)
+    SENT = 0x7F7F
+
+    def run(chunks):
+        roll = np.zeros((3, 4, 2 * DI), np.uint16)
+        pk = np.full((3, 6, DI), SENT, np.uint16)
+        done = np.zeros(3, np.int32)
+        for c in chunks:
+            take = np.minimum(c, n - done)
+            kg = np.zeros((3, max(1, int(take.max())), 2 * DI), np.uint16)
+            for s_ in range(3):
+                kg[s_, :take[s_]] = cells[s_, done[s_]:done[s_] + take[s_]]
+            O.pool_append(done, take, kg, roll, pk, pos, L=L)
+            done += take
+        assert np.array_equal(done, n)
+        return roll, pk
+
+    r1, p1 = run([np.ones(3, np.int32)] * 23)
+    r2, p2 = run([np.array([5, 2, 1]), np.array([7, 9, 1]), np.array([11, 3, 1])])
+    r3, p3 = run([n.copy()])
+    assert np.array_equal(r1, r2) and np.array_equal(r1, r3)
+    assert np.array_equal(p1, p2) and np.array_equal(p1, p3)
+    for s_ in range(3):
+        for p_ in range(6):
+            if p_ < n[s_] // 4:
+                c4 = cells[s_, 4 * p_:4 * p_ + 4]
+                assert np.array_equal(p1[s_, p_], _pool_one(L, fl(c4[:, :DI]), fl(c4[:, DI:]), pos))
+            else:
+                assert (p1[s_, p_] == SENT).all()
+        for t in range(4 * (n[s_] // 4), n[s_]):
+            assert np.array_equal(r1[s_, t % 4], cells[s_, t])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -34,6 +34,15 @@ MUTANTS = [
     ("query_head_transposed", "q + ((int64_t)qq * n_heads + h) * D;", "q + ((int64_t)h * n_q + qq) * D;"),
     ("seq_ignored_in_attend", "const int64_t seq = q_seq ? q_seq[qq] : qq;", "const int64_t seq = 0;"),
     ("pool_expand_wrong", "dst[count++] = (int32_t)(pick[i] * kpool + j);", "dst[count++] = (int32_t)(pick[i] + j);"),
+    ("pool_no_position_embedding", "+ (double)pos_emb[j * d_idx + d];", "+ 0.0;"),
+    ("pool_position_slot_reversed", "(double)pos_emb[j * d_idx + d];", "(double)pos_emb[(3 - j) * d_idx + d];"),
+    ("pool_one_logit_per_slot", "a[j] = bf16_value(c[j][d_idx + d]) + (double)pos_emb[j * d_idx + d];",
+     "a[j] = bf16_value(c[j][d_idx]) + (double)pos_emb[j * d_idx];"),
+    ("pool_gate_as_value", "num += e * bf16_value(c[j][d]);", "num += e * bf16_value(c[j][d_idx + d]);"),
+    ("pool_not_normalised", "out[d] = bf16_from_double(num / den);", "out[d] = bf16_from_double(num / 4.0);"),
+    ("pool_complete_on_slot_0", "if (slot == 3) {", "if (slot == 0) {"),
+    ("pool_index_off", "t / 4) * d_idx);", "(t / 4 + (t >= 8))) * d_idx);"),
+    ("pool_round_truncates", "const double r = rint(ldexp(m, 8));", "const double r = trunc(ldexp(m, 8));"),
 ]
 
 
