@@ -118,6 +118,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=6.0)
+    ap.add_argument("--producer", action="store_true",
+                    help="time the k-pool key producer instead: one bulk append of 2^20 - 1 tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (to scale byte counters)")
     args = ap.parse_args()
@@ -125,6 +127,9 @@ def main() -> int:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(the multi-GPU sharding is a design note, not an implementation)", file=sys.stderr)
         return 2
+
+    if args.producer:
+        return run_producer(args)
 
     import torch
     from deepseek_sparse_attention_amd import binding as B
@@ -229,6 +234,66 @@ def main() -> int:
         del reps
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_producer(args) -> int:
+    """k-pool key producer on the k-pool buffer size: one sequence, 2^20 - 1
+    tokens appended at once (262,143 pools); cells are 512 B (key | gate),
+    pool keys 256 B.  Inputs resident in HBM; 4 replicas rotated."""
+    import torch
+    from deepseek_sparse_attention_amd import binding as B
+
+    torch.cuda.set_device(0)
+    B.device_check()
+    T = (1 << 20) - 1
+    P = T // 4
+    g = torch.Generator(device="cpu").manual_seed(20261202)
+    pos = torch.randn((4, 128), generator=g).cuda()
+    reps = []
+    for r in range(max(1, args.replicas)):
+        cells = (torch.randn((1, T, 256), generator=g) * 2).to(torch.bfloat16).view(torch.int16).cuda()
+        reps.append(cells)
+    n_tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n_new = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    roll = torch.zeros((1, 4, 256), dtype=torch.int16, device="cuda")
+    keys = torch.empty((1, P, 128), dtype=torch.int16, device="cuda")
+    R = len(reps)
+    for i in range(args.warmup):
+        B.pool_append(n_tok, n_new, T, reps[i % R], roll, keys, pos)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        B.pool_append(n_tok, n_new, T, reps[i % R], roll, keys, pos)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / args.steps
+    nbytes = T * 512 + P * 256
+    gbps = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": "k-pool key producer: pool keys per second (bulk append of 2^20 - 1 tokens)",
+        "value": round(P / (us * 1e-6), 1), "unit": "pool keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 math, bf16 out", "data": "synthetic",
+        "config": {"workload": f"k-pool producer: 1 sequence, {T} tokens appended, {P} pools", "replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "k_pool_append", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        n = 1 << 16
+        cells = reps[0][:, :n].cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        O.pool_append(np.zeros(1, np.int32), np.array([n], np.int32), cells,
+                      np.zeros((1, 4, 256), np.uint16), np.zeros((1, n // 4, 128), np.uint16),
+                      pos.cpu().numpy())
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round((n // 4) / el, 1), "unit": "pool keys/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} tokens ({n // 4} pools) of the same buffer, "
+                                                           f"{el:.2f} s, one thread (the producer oracle is serial)"}
     print(json.dumps(res), flush=True)
     return 0
 

@@ -28,7 +28,8 @@ class Batch(ctypes.Structure):
 
 
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
-           "dsa_decode_step", "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events")
+           "dsa_decode_step", "dsa_pool_append", "dsa_status_str", "dsa_last_error", "dsa_device_check",
+           "dsa_set_timing_events")
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -44,6 +45,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_topk": (ctypes.c_int, [G, B, P, i64, P, i32, P, P, sz, P]),
         "dsa_mla_attend": (ctypes.c_int, [G, B, P, P, i64, P, i32, P, P, P, P, sz, P]),
         "dsa_decode_step": (ctypes.c_int, [G, B, P, P, P, i64, P, P, i64, P, i32, P, P, P, P, sz, P]),
+        "dsa_pool_append": (ctypes.c_int, [i32, P, P, i32, P, i64, P, P, i64, P, P]),
         "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_device_check": (ctypes.c_int, []),
@@ -140,6 +142,24 @@ def decode_step(geom: dict, b: Batch, idx_q, idx_w, idx_k, key_seq_stride: int, 
                                 _ptr(idx_k), int(key_seq_stride), _ptr(q), _ptr(cache), int(cache_seq_stride),
                                 _ptr(sel), int(sel_ld), _ptr(sel_count), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream)), "dsa_decode_step")
+
+
+def pool_append(n_tok, n_new, max_new: int, new_kg, rolling, pool_keys, pos_emb, stream=None) -> None:
+    """k-pool key producer.  n_tok, n_new: int32 [n_seq]; new_kg: bf16 bits
+    (int16/uint16) [n_seq, new_stride, 256]; rolling [n_seq, 4, 256];
+    pool_keys [n_seq, pool_stride, 128]; pos_emb float32 [4, 128]; all cuda."""
+    for t, dt in ((n_tok, torch.int32), (n_new, torch.int32), (pos_emb, torch.float32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"expected a contiguous cuda {dt} tensor, got {t.dtype} on {t.device}")
+    for t in (new_kg, rolling, pool_keys):
+        if t.element_size() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("cells, rolling buffer and pool keys are contiguous 16-bit cuda tensors")
+    n_seq = int(n_tok.shape[0])
+    if new_kg.shape[0] != n_seq or rolling.shape != (n_seq, 4, 256) or pool_keys.shape[0] != n_seq:
+        raise ValueError("shapes: new_kg [n_seq, stride, 256], rolling [n_seq, 4, 256], pool_keys [n_seq, P, 128]")
+    _check(_lib.dsa_pool_append(n_seq, _ptr(n_tok), _ptr(n_new), int(max_new), _ptr(new_kg), int(new_kg.shape[1]),
+                                _ptr(rolling), _ptr(pool_keys), int(pool_keys.shape[1]), _ptr(pos_emb),
+                                _stream(stream)), "dsa_pool_append")
 
 
 def set_timing_events(events) -> None:

@@ -24,6 +24,7 @@ hipError_t launch_hist(const Args &a, hipStream_t st);
 hipError_t launch_filter(const Args &a, hipStream_t st);
 hipError_t launch_select(const Args &a, hipStream_t st);
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
+hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
 }  // namespace dsa
 
 namespace {
@@ -345,6 +346,36 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
         DSA_TRY(launched(dsa::launch_attend(a, stream, [&] { tm.tick(); }), "attend"));
         tm.tick();
         return (int)DSA_OK;
+    });
+}
+
+int dsa_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new, int32_t max_new,
+                    const dsa_bf16 *new_kg, int64_t new_stride, dsa_bf16 *rolling, dsa_bf16 *pool_keys,
+                    int64_t pool_stride, const float *pos_emb, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        if (n_seq < 1) return fail(DSA_ERR_ARG, "n_seq < 1");
+        if (max_new < 0) return fail(DSA_ERR_ARG, "max_new < 0");
+        if (new_stride < (max_new > 0 ? max_new : 1)) return fail(DSA_ERR_ARG, "new_stride < max_new");
+        if (pool_stride < 1) return fail(DSA_ERR_ARG, "pool_stride < 1");
+        if (!n_tok || !n_new || !new_kg || !rolling || !pool_keys || !pos_emb)
+            return fail(DSA_ERR_ARG, "NULL pointer");
+        if (!aligned16(n_tok) || !aligned16(n_new) || !aligned16(new_kg) || !aligned16(rolling) ||
+            !aligned16(pool_keys) || !aligned16(pos_emb))
+            return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::PoolArgs a;
+        a.n_seq = n_seq;
+        a.n_tok = n_tok;
+        a.n_new = n_new;
+        a.max_new = max_new;
+        a.new_kg = new_kg;
+        a.new_stride = new_stride;
+        a.rolling = rolling;
+        a.pool_keys = pool_keys;
+        a.pool_stride = pool_stride;
+        a.pos_emb = pos_emb;
+        return launched(dsa::launch_pool_append(a, stream), "pool_append");
     });
 }
 

@@ -42,4 +42,17 @@ struct Args {
     int32_t pf_run;       // queries per run (>= 2 when prefill)
 };
 
+// Arguments of the k-pool key producer.
+struct PoolArgs {
+    int32_t n_seq;
+    const int32_t *n_tok, *n_new;  // per sequence: tokens held, tokens appended now
+    int64_t max_new;               // host bound of n_new
+    const uint16_t *new_kg;        // [n_seq][new_stride][2 * 128] key|gate cells
+    int64_t new_stride;
+    uint16_t *rolling;             // [n_seq][4][2 * 128]
+    uint16_t *pool_keys;           // [n_seq][pool_stride][128]
+    int64_t pool_stride;
+    const float *pos_emb;          // [4][128]
+};
+
 }  // namespace dsa

@@ -1264,6 +1264,76 @@ __global__ __launch_bounds__(128) void k_reduce(Args a) {
         a.lse[(size_t)q * kHeads + h] = bad ? NAN : (M + __log2f(L)) * 0.69314718055994531f;
 }
 
+// ---------------------------------------------------------------- pool keys
+// k-pool key producer ("GLM-5.3-Flash on WASTE", "DeepSeek Sparse Attention,
+// k-pool flavour": one 128-wide key per pool of four tokens, computed when
+// the pool's last token arrives, beside a rolling buffer of the pool being
+// filled; TensorSharp2 "GLM-5.3-Flash (glm5next)": [key|gate] per cell, a
+// softmax over the gates plus a per-slot position embedding compresses the
+// pool).  Per key dimension d:
+//   K[d] = sum_j softmax_j(gate_j[d] + E[j][d]) * key_j[d],  j over the 4 slots,
+// in fp32, stored as bf16 rounded to nearest even.
+// grid (ceil(pools per call / 4), n_seq), 256 threads: wave w of block b
+// compresses pool n_tok / 4 + 4 b + w of its sequence if the call completes
+// it; lane l takes dimensions 2l and 2l + 1.  Block 0 then moves the cells of
+// the pool left incomplete into the rolling buffer (its wave 0 is the only
+// reader of that buffer, so the barrier orders the reads before the writes).
+constexpr int kCell = 2 * kIdxDim;   // bf16 per cell: key, then gate
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void k_pool_append(PoolArgs a) {
+    const int s = blockIdx.y, w = threadIdx.x >> 6, lane = lane_id();
+    const int64_t n_tok = a.n_tok[s], n_new = a.n_new[s];
+    if (n_tok < 0 || n_new < 0 || n_new > a.max_new) return;
+    const int64_t end = n_tok + n_new;
+    const int64_t p0 = n_tok / 4, p1 = end / 4;     // pools [p0, p1) complete after the call
+    const uint16_t *roll = a.rolling + (size_t)s * 4 * kCell;
+    const uint16_t *nk = a.new_kg + (size_t)s * a.new_stride * kCell;
+    const int64_t p = p0 + 4 * (int64_t)blockIdx.x + w;
+    if (p < p1 && p < a.pool_stride) {
+        float key[4][2], lg[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t t = 4 * p + j;
+            const uint16_t *c = t < n_tok ? roll + j * kCell : nk + (t - n_tok) * kCell;
+            const uint32_t kv = *(const uint32_t *)(c + 2 * lane);
+            const uint32_t gv = *(const uint32_t *)(c + kIdxDim + 2 * lane);
+            key[j][0] = __uint_as_float(kv << 16);
+            key[j][1] = __uint_as_float(kv & 0xFFFF0000u);
+            lg[j][0] = __uint_as_float(gv << 16) + a.pos_emb[j * kIdxDim + 2 * lane];
+            lg[j][1] = __uint_as_float(gv & 0xFFFF0000u) + a.pos_emb[j * kIdxDim + 2 * lane + 1];
+        }
+        uint32_t packed = 0;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const float m = fmaxf(fmaxf(lg[0][h], lg[1][h]), fmaxf(lg[2][h], lg[3][h]));
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float e = __builtin_amdgcn_exp2f((lg[j][h] - m) * 1.4426950408889634f);
+                num += e * key[j][h];
+                den += e;
+            }
+            packed |= (uint32_t)bf16_rne(num / den) << (16 * h);
+        }
+        *(uint32_t *)(a.pool_keys + ((size_t)s * a.pool_stride + p) * kIdxDim + 2 * lane) = packed;
+    }
+    if (blockIdx.x != 0) return;
+    __syncthreads();
+    // cells of the incomplete pool that arrived in this call
+    uint16_t *rw = a.rolling + (size_t)s * 4 * kCell;
+    for (int64_t t = (4 * p1 > n_tok ? 4 * p1 : n_tok) + w; t < end; t += 4) {
+        const uint32_t *src = (const uint32_t *)(nk + (t - n_tok) * kCell);
+        uint32_t *dst = (uint32_t *)(rw + (t % 4) * kCell);
+        dst[lane] = src[lane];
+        dst[64 + lane] = src[64 + lane];
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
     const size_t words = bytes / 4;
@@ -1320,4 +1390,13 @@ hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void
     return hipGetLastError();
 }
 
+}  // namespace dsa
+
+namespace dsa {
+hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st) {
+    const int64_t pools = (a.max_new + 3) / 4;
+    const unsigned gx = (unsigned)((pools + 3) / 4 > 0 ? (pools + 3) / 4 : 1);
+    hipLaunchKernelGGL(k_pool_append, dim3(gx, a.n_seq), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 }  // namespace dsa

@@ -174,6 +174,34 @@ int dsa_decode_step(const dsa_geometry *geom, const dsa_batch *batch,
                     float *out, float *lse,
                     void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* 5. k-pool key producer ("GLM-5.3-Flash on WASTE", "DeepSeek Sparse
+ * Attention, k-pool flavour"; TensorSharp2 "GLM-5.3-Flash (glm5next)").
+ * A cell is a token's indexer key followed by its gate, 2 x 128 bf16.
+ * For each sequence s, which holds n_tok[s] tokens, appends n_new[s] tokens
+ * whose cells are new_kg[s][0 .. n_new[s]).  Token t goes to rolling slot
+ * t mod 4, and every pool that the call completes (pool p = tokens
+ * 4p .. 4p+3) gets its key, per dimension d:
+ *   pool_keys[s][p][d] = bf16( sum_j softmax_j(gate_j[d] + pos_emb[j][d]) * key_j[d] )
+ * computed in fp32 and rounded to nearest even.  Cells of a pool that began
+ * before the call are read from the rolling buffer; afterwards slots
+ * 0 .. (end mod 4) - 1 hold the cells of each sequence's incomplete pool
+ * (end = n_tok + n_new), and the other slots are unspecified.
+ *   n_tok, n_new  device int32 [n_seq]; a sequence with n_tok < 0, n_new < 0
+ *                 or n_new > max_new is left untouched
+ *   max_new       host bound of n_new (sizes the grid); new_stride >= max_new
+ *   new_kg        device bf16 [n_seq][new_stride][256]
+ *   rolling       device bf16 [n_seq][4][256], read and written; its cells
+ *                 of tokens < n_tok must be those of the current pool
+ *   pool_keys     device bf16 [n_seq][pool_stride][128]; pools at or past
+ *                 pool_stride are not written
+ *   pos_emb       device fp32 [4][128]
+ * All pointers 16-byte aligned.  No workspace.  Errors as for the calls
+ * above. */
+int dsa_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new, int32_t max_new,
+                    const dsa_bf16 *new_kg, int64_t new_stride,
+                    dsa_bf16 *rolling, dsa_bf16 *pool_keys, int64_t pool_stride,
+                    const float *pos_emb, hipStream_t stream);
+
 /* Instrumentation for benchmarks.  With events set (n_events > 0), each
  * dsa_decode_step call on this thread records events[0] on its stream before
  * its first kernel and events[i + 1] after its i-th kernel (as many as fit),
