@@ -363,3 +363,63 @@ int oracle_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new
     }
     return 0;
 }
+
+/*
+ * Absorption of the per-head key and value up-projections ("GLM 5.2 in pure
+ * C", section "Attention: Multi head Latent Attention With a Tiny KV Cache":
+ * by linearity q . k_nope = (W_K^T q) . L, so the query absorbs the key
+ * up-projection once, scores are dots against the latent, and the pooled
+ * latent is projected back out per head at the end; TensorSharp2 table "The
+ * block": the K/V decompression is folded into the query and the output).
+ *
+ *   q_abs[m][h][n]        = sum_{k < d_nope} q_nope[m][h][k] * w_uk[h][k][n]   (n < d_latent)
+ *   q_abs[m][h][d_latent + r] = q_rope[m][h][r]                               (r < d_rope)
+ *   ctx[m][h][i]          = sum_{j < d_latent} o[m][h][j] * w_uv[h][i][j]      (i < d_v)
+ *
+ * q_abs is stored as bf16 (nearest, ties to even, from the double sum); ctx
+ * as float.  Weight layouts follow the model's up-projection rows: w_uk
+ * [H][d_nope][d_latent] (row k of head h), w_uv [H][d_v][d_latent].
+ */
+int oracle_absorb_query(int32_t n_q, int32_t n_heads, int32_t d_nope, int32_t d_latent, int32_t d_rope,
+                        const uint16_t *q_nope, const uint16_t *q_rope, const uint16_t *w_uk,
+                        uint16_t *q_abs)
+{
+    const int64_t D = d_latent + d_rope;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t m = 0; m < n_q; m++) {
+        for (int32_t h = 0; h < n_heads; h++) {
+            const uint16_t *qn = q_nope + ((int64_t)m * n_heads + h) * d_nope;
+            const uint16_t *W = w_uk + (int64_t)h * d_nope * d_latent;
+            uint16_t *dst = q_abs + ((int64_t)m * n_heads + h) * D;
+            for (int32_t n = 0; n < d_latent; n++) {
+                double acc = 0.0;
+                for (int32_t k = 0; k < d_nope; k++)
+                    acc += bf16_value(qn[k]) * bf16_value(W[(int64_t)k * d_latent + n]);
+                dst[n] = bf16_from_double(acc);
+            }
+            for (int32_t r = 0; r < d_rope; r++)
+                dst[d_latent + r] = q_rope[((int64_t)m * n_heads + h) * d_rope + r];
+        }
+    }
+    return 0;
+}
+
+int oracle_project_output(int32_t n_q, int32_t n_heads, int32_t d_latent, int32_t d_v,
+                          const float *o, const uint16_t *w_uv, float *ctx)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t m = 0; m < n_q; m++) {
+        for (int32_t h = 0; h < n_heads; h++) {
+            const float *oh = o + ((int64_t)m * n_heads + h) * d_latent;
+            const uint16_t *W = w_uv + (int64_t)h * d_v * d_latent;
+            float *dst = ctx + ((int64_t)m * n_heads + h) * d_v;
+            for (int32_t i = 0; i < d_v; i++) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < d_latent; j++)
+                    acc += (double)oh[j] * bf16_value(W[(int64_t)i * d_latent + j]);
+                dst[i] = (float)acc;
+            }
+        }
+    }
+    return 0;
+}

@@ -40,6 +40,8 @@ def load(path: str):
                                      P, P, P, i64, P, P, i64, P, i32, P, P, P]
     L.oracle_max_threads.argtypes = []
     L.oracle_pool_append.argtypes = [i32, P, P, P, i64, i32, P, P, i64, P]
+    L.oracle_absorb_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+    L.oracle_project_output.argtypes = [i32, i32, i32, i32, P, P, P]
     for f in (L.oracle_index_scores, L.oracle_topk, L.oracle_mla_attend,
               L.oracle_decode_step, L.oracle_max_threads):
         f.restype = ctypes.c_int
@@ -161,3 +163,32 @@ def pool_append(n_tok, n_new, new_kg, rolling, pool_keys, pos_emb, L=None):
                                          _p(rolling), _p(pool_keys), pool_keys.shape[1], _p(pos_emb))
     assert rc == 0
     return rolling, pool_keys
+
+
+def absorb_query(q_nope, q_rope, w_uk, L=None):
+    """q_abs (uint16 bf16 [n_q, H, d_latent + d_rope]) from q_nope [n_q, H, d_nope],
+    q_rope [n_q, H, d_rope] (or None for d_rope 0) and w_uk [H, d_nope, d_latent]."""
+    q_nope, w_uk = _c(q_nope, np.uint16), _c(w_uk, np.uint16)
+    n_q, H, dn = q_nope.shape
+    assert w_uk.shape[:2] == (H, dn)
+    dl = w_uk.shape[2]
+    if q_rope is None:
+        q_rope = np.zeros((n_q, H, 0), np.uint16)
+    q_rope = _c(q_rope, np.uint16)
+    dr = q_rope.shape[2]
+    out = np.empty((n_q, H, dl + dr), np.uint16)
+    rc = (L or lib()).oracle_absorb_query(n_q, H, dn, dl, dr, _p(q_nope), _p(q_rope), _p(w_uk), _p(out))
+    assert rc == 0
+    return out
+
+
+def project_output(o, w_uv, L=None):
+    """ctx (float32 [n_q, H, d_v]) from o float32 [n_q, H, d_latent] and w_uv [H, d_v, d_latent]."""
+    o, w_uv = _c(o, np.float32), _c(w_uv, np.uint16)
+    n_q, H, dl = o.shape
+    assert w_uv.shape[0] == H and w_uv.shape[2] == dl
+    dv = w_uv.shape[1]
+    out = np.empty((n_q, H, dv), np.float32)
+    rc = (L or lib()).oracle_project_output(n_q, H, dl, dv, _p(o), _p(w_uv), _p(out))
+    assert rc == 0
+    return out

@@ -447,4 +447,107 @@ def pin_pool_append_semantics(L):
             assert np.array_equal(r1[s_, t % 4], cells[s_, t])
 
 
+# ---------------------------------------------------------------- absorption
+DN, DL, DV = 256, 512, 256
+
+
+def _sparse_unit(rng, shape, density):
+    """Entries in {-1, 0, 1}, mostly 0: sums stay small integers, exact in bf16."""
+    v = rng.integers(-1, 2, size=shape) * (rng.random(shape) < density)
+    return v.astype(np.float32)
+
+
+def pin_absorb_is_the_key_identity(L):
+    """By linearity q . (W L) = (W^T q) . L: the absorbed query dotted with a
+    latent row equals the query dotted with the decompressed key, computed
+    here by numpy integer matmuls (small integers, so every value is exact)."""
+    rng = np.random.default_rng(41)
+    n_q, Hh, T = 3, 4, 9
+    qn = _sparse_unit(rng, (n_q, Hh, DN), 0.05)
+    W = _sparse_unit(rng, (Hh, DN, DL), 0.01)
+    Lat = rng.integers(-3, 4, size=(T, DL)).astype(np.int64)
+    qa = fl(O.absorb_query(bf(qn), None, bf(W), L=L))                    # [n_q, H, DL]
+    assert np.array_equal(qa, np.einsum("mhk,hkn->mhn", qn.astype(np.int64), W.astype(np.int64)))
+    keys = np.einsum("hkn,tn->htk", W.astype(np.int64), Lat)              # decompressed keys
+    for m in range(n_q):
+        for h in range(Hh):
+            assert np.array_equal(qa[m, h].astype(np.int64) @ Lat.T, keys[h] @ qn[m, h].astype(np.int64))
+
+
+def pin_absorb_selection_and_rope(L):
+    """W = [I | 0] puts q_nope in the first 256 latent dimensions; the RoPE
+    part is appended unchanged after the 512 latent dimensions."""
+    rng = np.random.default_rng(42)
+    qn = bf(rng.standard_normal((2, 3, DN)))
+    qr = bf(rng.standard_normal((2, 3, 64)))
+    W = np.zeros((3, DN, DL), np.float32)
+    W[:, np.arange(DN), np.arange(DN)] = 1.0
+    qa = O.absorb_query(qn, qr, bf(W), L=L)
+    assert np.array_equal(qa[:, :, :DN], qn) and (fl(qa[:, :, DN:DL]) == 0).all()
+    assert np.array_equal(qa[:, :, DL:], qr)
+
+
+def pin_absorb_rounding(L):
+    """The absorbed query is the nearest bf16 of the exact sum, ties to even:
+    1 + 2^-7 + 2^-9 -> 1 + 2^-7; 1 + 2^-7 + 3*2^-9 -> 1 + 2^-6; and the tie
+    1 + 2^-7 + 2^-8 -> 1 + 2^-6 (even)."""
+    def one(extra):
+        qn = np.zeros((1, 1, DN), np.float32)
+        qn[0, 0, :2] = [1.0, 1.0]
+        W = np.zeros((1, DN, DL), np.float32)
+        W[0, 0, 0] = 1.0 + 2.0 ** -7
+        W[0, 1, 0] = extra
+        return float(fl(O.absorb_query(bf(qn), None, bf(W), L=L))[0, 0, 0])
+    assert one(2.0 ** -9) == 1.0 + 2.0 ** -7
+    assert one(3 * 2.0 ** -9) == 1.0 + 2.0 ** -6
+    assert one(2.0 ** -8) == 1.0 + 2.0 ** -6
+
+
+def pin_project_selection_and_linearity(L):
+    """W_UV = [I | 0] returns the first 256 latent columns; the projection is
+    linear (exact for integer-valued inputs) and matches float64 matmul."""
+    rng = np.random.default_rng(43)
+    o = rng.standard_normal((2, 3, DL)).astype(np.float32)
+    W = np.zeros((3, DV, DL), np.float32)
+    W[:, np.arange(DV), np.arange(DV)] = 1.0
+    assert np.array_equal(O.project_output(o, bf(W), L=L), o[:, :, :DV])
+    oi = rng.integers(-8, 9, size=(2, 3, DL)).astype(np.float32)
+    oj = rng.integers(-8, 9, size=(2, 3, DL)).astype(np.float32)
+    Wi = bf(rng.integers(-4, 5, size=(3, DV, DL)))
+    assert np.array_equal(O.project_output(oi + oj, Wi, L=L),
+                          O.project_output(oi, Wi, L=L) + O.project_output(oj, Wi, L=L))
+    Wr = bf(rng.standard_normal((3, DV, DL)))
+    ref = np.einsum("mhj,hij->mhi", o.astype(np.float64), fl(Wr))
+    assert np.allclose(O.project_output(o, Wr, L=L), ref, rtol=1e-6, atol=1e-5)
+
+
+def pin_absorbed_attention_is_explicit_mla(L):
+    """Absorbed decode equals explicit MLA: per head, keys k_t = W_UK L_t and
+    values v_t = W_UV L_t decompressed from the latent, scores
+    (q_nope . k_t + q_rope . rope_t) / 16, softmax, output sum_t p_t v_t
+    (float64 numpy; the absorbed path rounds q_abs to bf16, hence the
+    tolerance)."""
+    rng = np.random.default_rng(44)
+    Hh, T, n_q = 64, 12, 2
+    qn = bf(rng.standard_normal((n_q, Hh, DN)) * 0.5)
+    qr = bf(rng.standard_normal((n_q, Hh, 64)))
+    Wk = bf(rng.standard_normal((Hh, DN, DL)) * 0.05)
+    Wv = bf(rng.standard_normal((Hh, DV, DL)) * 0.05)
+    C = bf(rng.standard_normal((1, T, DL + 64)))
+    qa = O.absorb_query(qn, qr, Wk, L=L)
+    sel = np.tile(np.arange(T, dtype=np.int32), (n_q, 1))
+    o, _ = O.mla_attend(np.zeros(n_q, np.int32), DL, 64, 1 / 16, qa, C, sel, np.full(n_q, T, np.int32), L=L)
+    ctx = O.project_output(o, Wv, L=L)
+    Lt, rope = fl(C[0, :, :DL]), fl(C[0, :, DL:])
+    for m in range(n_q):
+        for h in range(Hh):
+            k = Lt @ fl(Wk[h]).T                                 # [T, DN]
+            v = Lt @ fl(Wv[h]).T                                 # [T, DV]
+            z = (k @ fl(qn[m, h]) + rope @ fl(qr[m, h])) / 16
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            want = p @ v
+            assert np.allclose(ctx[m, h], want, rtol=2e-3, atol=2e-3 * np.abs(want).max())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -43,6 +43,15 @@ MUTANTS = [
     ("pool_complete_on_slot_0", "if (slot == 3) {", "if (slot == 0) {"),
     ("pool_index_off", "t / 4) * d_idx);", "(t / 4 + (t >= 8))) * d_idx);"),
     ("pool_round_truncates", "const double r = rint(ldexp(m, 8));", "const double r = trunc(ldexp(m, 8));"),
+    ("absorb_weight_transposed", "bf16_value(W[(int64_t)k * d_latent + n]);", "bf16_value(W[(int64_t)n * d_nope + k]);"),
+    ("absorb_last_term_dropped", "for (int32_t k = 0; k < d_nope; k++)\n                    acc += bf16_value(qn[k])",
+     "for (int32_t k = 0; k < d_nope - 1; k++)\n                    acc += bf16_value(qn[k])"),
+    ("absorb_rope_dropped", "dst[d_latent + r] = q_rope[((int64_t)m * n_heads + h) * d_rope + r];", "dst[d_latent + r] = 0;"),
+    ("absorb_wrong_head_weight", "const uint16_t *W = w_uk + (int64_t)h * d_nope * d_latent;", "const uint16_t *W = w_uk;"),
+    ("project_weight_transposed", "bf16_value(W[(int64_t)i * d_latent + j]);", "bf16_value(W[(int64_t)j * d_v + i]);"),
+    ("project_wrong_head_weight", "const uint16_t *W = w_uv + (int64_t)h * d_v * d_latent;", "const uint16_t *W = w_uv;"),
+    ("project_half_the_latent", "for (int32_t j = 0; j < d_latent; j++)\n                    acc += (double)oh[j]",
+     "for (int32_t j = 0; j < d_latent / 2; j++)\n                    acc += (double)oh[j]"),
 ]
 
 
