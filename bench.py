@@ -120,6 +120,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=6.0)
     ap.add_argument("--producer", action="store_true",
                     help="time the k-pool key producer instead: one bulk append of 2^20 - 1 tokens")
+    ap.add_argument("--absorb", action="store_true",
+                    help="time the absorption GEMMs instead (absorb + project, 8 and 512 queries)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (to scale byte counters)")
     args = ap.parse_args()
@@ -130,6 +132,8 @@ def main() -> int:
 
     if args.producer:
         return run_producer(args)
+    if args.absorb:
+        return run_absorb(args)
 
     import torch
     from deepseek_sparse_attention_amd import binding as B
@@ -294,6 +298,81 @@ def run_producer(args) -> int:
         res["cpu_baseline"] = {"value": round((n // 4) / el, 1), "unit": "pool keys/s", "cores": 1,
                                "kind": "oracle", "sample": f"{n} tokens ({n // 4} pools) of the same buffer, "
                                                            f"{el:.2f} s, one thread (the producer oracle is serial)"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_absorb(args) -> int:
+    """Absorption GEMMs (absorb the key up-projection into the query, project
+    the attention output through the value up-projection), 64 heads, bf16
+    weights [64][256][512] each.  Timed for a decode batch of 8 queries (the
+    32 MiB of weights dominate: HBM-bound) and a 512-query prefill chunk
+    (MFMA-bound); 4 weight replicas rotated."""
+    import torch
+    from deepseek_sparse_attention_amd import binding as B
+
+    torch.cuda.set_device(0)
+    B.device_check()
+    g = torch.Generator(device="cpu").manual_seed(20261202)
+    R = max(1, args.replicas)
+    wk = [(torch.randn((64, 256, 512), generator=g) * 0.05).to(torch.bfloat16).view(torch.int16).cuda() for _ in range(R)]
+    wv = [(torch.randn((64, 256, 512), generator=g) * 0.05).to(torch.bfloat16).view(torch.int16).cuda() for _ in range(R)]
+
+    def timed(n_q):
+        qn = torch.randn((n_q, 64, 256), generator=g).to(torch.bfloat16).view(torch.int16).cuda()
+        qr = torch.randn((n_q, 64, 64), generator=g).to(torch.bfloat16).view(torch.int16).cuda()
+        qa = torch.empty((n_q, 64, 576), dtype=torch.int16, device="cuda")
+        o = torch.randn((n_q, 64, 512), generator=g).cuda()
+        ctx = torch.empty((n_q, 64, 256), device="cuda")
+        for i in range(args.warmup):
+            B.absorb_query(qn, qr, wk[i % R], qa)
+            B.project_output(o, wv[i % R], ctx)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for i in range(args.steps):                      # back to back, weights rotated
+            B.absorb_query(qn, qr, wk[i % R], qa)
+        ev[1].record()
+        for i in range(args.steps):
+            B.project_output(o, wv[i % R], ctx)
+        ev[2].record()
+        torch.cuda.synchronize()
+        ta = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+        tp = ev[1].elapsed_time(ev[2]) * 1e3 / args.steps
+        wbytes = 64 * 256 * 512 * 2
+        b_abs = wbytes + n_q * 64 * (256 + 64 + 576) * 2
+        b_prj = wbytes + n_q * 64 * (512 + 256) * 4
+        fl = 2 * n_q * 64 * 256 * 512
+        return {"queries": n_q, "absorb_us": round(ta, 2), "project_us": round(tp, 2),
+                "absorb_GBps": round(b_abs / (ta * 1e-6) / 1e9, 1), "project_GBps": round(b_prj / (tp * 1e-6) / 1e9, 1),
+                "absorb_TFLOPs": round(fl / (ta * 1e-6) / 1e12, 1), "project_TFLOPs": round(fl / (tp * 1e-6) / 1e12, 1),
+                "bytes": b_abs + b_prj, "flops": 2 * fl}
+
+    dec, pre = timed(8), timed(512)
+    us = dec["absorb_us"] + dec["project_us"]
+    gbps = dec["bytes"] / (us * 1e-6) / 1e9
+    res = {
+        "metric": "absorption GEMMs (absorb + project), decode batch of 8 queries per second",
+        "value": round(8 / (us * 1e-6), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "absorb q_nope 256 -> 512 and project o 512 -> 256 per head, 64 heads, "
+                               "bf16 weights [64][256][512] x 2", "replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "k_absorb + k_project", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": dec["bytes"]},
+        "decode_8": dec, "prefill_512": pre,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        rng = np.random.default_rng(1)
+        qn = rng.integers(-3, 4, size=(8, 64, 256)).astype(np.uint16)
+        t0 = time.perf_counter()
+        O.absorb_query(qn, None, wk[0].cpu().numpy().view(np.uint16))
+        O.project_output(rng.standard_normal((8, 64, 512)).astype(np.float32), wv[0].cpu().numpy().view(np.uint16))
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(8 / el, 1), "unit": "queries/s", "cores": O.max_threads(),
+                               "kind": "oracle", "sample": f"one decode batch of 8 queries, {el:.2f} s"}
     print(json.dumps(res), flush=True)
     return 0
 

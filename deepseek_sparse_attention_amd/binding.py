@@ -28,7 +28,7 @@ class Batch(ctypes.Structure):
 
 
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
-           "dsa_decode_step", "dsa_pool_append", "dsa_status_str", "dsa_last_error", "dsa_device_check",
+           "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_status_str", "dsa_last_error", "dsa_device_check",
            "dsa_set_timing_events")
 
 
@@ -46,6 +46,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_mla_attend": (ctypes.c_int, [G, B, P, P, i64, P, i32, P, P, P, P, sz, P]),
         "dsa_decode_step": (ctypes.c_int, [G, B, P, P, P, i64, P, P, i64, P, i32, P, P, P, P, sz, P]),
         "dsa_pool_append": (ctypes.c_int, [i32, P, P, i32, P, i64, P, P, i64, P, P]),
+        "dsa_absorb_query": (ctypes.c_int, [i32, i32, P, P, P, P, P]),
+        "dsa_project_output": (ctypes.c_int, [i32, P, P, P, P]),
         "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_device_check": (ctypes.c_int, []),
@@ -160,6 +162,34 @@ def pool_append(n_tok, n_new, max_new: int, new_kg, rolling, pool_keys, pos_emb,
     _check(_lib.dsa_pool_append(n_seq, _ptr(n_tok), _ptr(n_new), int(max_new), _ptr(new_kg), int(new_kg.shape[1]),
                                 _ptr(rolling), _ptr(pool_keys), int(pool_keys.shape[1]), _ptr(pos_emb),
                                 _stream(stream)), "dsa_pool_append")
+
+
+def absorb_query(q_nope, q_rope, w_uk, q_abs, stream=None) -> None:
+    """q_nope [n_q, 64, 256], q_rope [n_q, 64, d_rope] or None, w_uk [64, 256, 512],
+    q_abs [n_q, 64, 512 + d_rope]: 16-bit (bf16 bits) contiguous cuda tensors."""
+    for t in (q_nope, w_uk, q_abs) + ((q_rope,) if q_rope is not None else ()):
+        if t.element_size() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("absorb_query takes contiguous 16-bit cuda tensors")
+    n_q = int(q_nope.shape[0])
+    d_rope = 0 if q_rope is None else int(q_rope.shape[2])
+    if tuple(q_nope.shape) != (n_q, 64, 256) or tuple(w_uk.shape) != (64, 256, 512) or \
+            tuple(q_abs.shape) != (n_q, 64, 512 + d_rope):
+        raise ValueError("shapes: q_nope [n_q, 64, 256], w_uk [64, 256, 512], q_abs [n_q, 64, 512 + d_rope]")
+    _check(_lib.dsa_absorb_query(n_q, d_rope, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(q_abs), _stream(stream)),
+           "dsa_absorb_query")
+
+
+def project_output(o, w_uv, ctx, stream=None) -> None:
+    """o float32 [n_q, 64, 512], w_uv 16-bit [64, 256, 512], ctx float32 [n_q, 64, 256]."""
+    n_q = int(o.shape[0])
+    if o.dtype != torch.float32 or ctx.dtype != torch.float32 or w_uv.element_size() != 2:
+        raise TypeError("project_output: o and ctx float32, w_uv 16-bit")
+    if tuple(o.shape) != (n_q, 64, 512) or tuple(w_uv.shape) != (64, 256, 512) or tuple(ctx.shape) != (n_q, 64, 256):
+        raise ValueError("shapes: o [n_q, 64, 512], w_uv [64, 256, 512], ctx [n_q, 64, 256]")
+    for t in (o, w_uv, ctx):
+        if not t.is_cuda or not t.is_contiguous():
+            raise TypeError("project_output takes contiguous cuda tensors")
+    _check(_lib.dsa_project_output(n_q, _ptr(o), _ptr(w_uv), _ptr(ctx), _stream(stream)), "dsa_project_output")
 
 
 def set_timing_events(events) -> None:

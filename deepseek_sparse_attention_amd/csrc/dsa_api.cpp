@@ -25,6 +25,8 @@ hipError_t launch_filter(const Args &a, hipStream_t st);
 hipError_t launch_select(const Args &a, hipStream_t st);
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
 hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
+hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st);
+hipError_t launch_project(const AbsorbArgs &a, hipStream_t st);
 }  // namespace dsa
 
 namespace {
@@ -376,6 +378,44 @@ int dsa_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new, i
         a.pool_stride = pool_stride;
         a.pos_emb = pos_emb;
         return launched(dsa::launch_pool_append(a, stream), "pool_append");
+    });
+}
+
+int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const dsa_bf16 *q_rope,
+                     const dsa_bf16 *w_uk, dsa_bf16 *q_abs, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        if (n_q < 1) return fail(DSA_ERR_ARG, "n_q < 1");
+        if (d_rope != 0 && d_rope != 64) return fail(DSA_ERR_UNSUPPORTED, "d_rope must be 0 or 64");
+        if (!q_nope || !w_uk || !q_abs || (d_rope && !q_rope)) return fail(DSA_ERR_ARG, "NULL pointer");
+        if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_abs) || (d_rope && !aligned16(q_rope)))
+            return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::AbsorbArgs a{};
+        a.n_q = n_q;
+        a.d_rope = d_rope;
+        a.q_nope = q_nope;
+        a.q_rope = q_rope;
+        a.w_uk = w_uk;
+        a.q_abs = q_abs;
+        return launched(dsa::launch_absorb(a, stream), "absorb");
+    });
+}
+
+int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float *ctx, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        if (n_q < 1) return fail(DSA_ERR_ARG, "n_q < 1");
+        if (!o || !w_uv || !ctx) return fail(DSA_ERR_ARG, "NULL pointer");
+        if (!aligned16(o) || !aligned16(w_uv) || !aligned16(ctx))
+            return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::AbsorbArgs a{};
+        a.n_q = n_q;
+        a.o = o;
+        a.w_uv = w_uv;
+        a.ctx = ctx;
+        return launched(dsa::launch_project(a, stream), "project");
     });
 }
 

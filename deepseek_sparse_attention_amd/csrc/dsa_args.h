@@ -55,4 +55,16 @@ struct PoolArgs {
     const float *pos_emb;          // [4][128]
 };
 
+// Arguments of the absorption GEMMs.
+struct AbsorbArgs {
+    int32_t n_q, d_rope;
+    const uint16_t *q_nope;  // [n_q][64][256]
+    const uint16_t *q_rope;  // [n_q][64][d_rope]
+    const uint16_t *w_uk;    // [64][256][512]
+    uint16_t *q_abs;         // [n_q][64][512 + d_rope]
+    const float *o;          // [n_q][64][512]
+    const uint16_t *w_uv;    // [64][256][512]
+    float *ctx;              // [n_q][64][256]
+};
+
 }  // namespace dsa

@@ -1334,6 +1334,134 @@ __global__ __launch_bounds__(256) void k_pool_append(PoolArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- absorption
+// The per-head key and value up-projections on either side of the attention
+// ("GLM 5.2 in pure C", "Attention: Multi head Latent Attention With a Tiny
+// KV Cache": the query absorbs the key up-projection once and the pooled
+// latent is projected back out per head; TensorSharp2 "The block"):
+//   q_abs[m][h][n] = bf16( sum_k q_nope[m][h][k] W_UK[h][k][n] ),  n < 512, then q_rope
+//   ctx[m][h][i]   = sum_j o[m][h][j] W_UV[h][i][j],                i < 256
+// Both as C^T = W' X^T on MFMA 16x16x32 bf16: A = 16 weight rows (output
+// features) x 32 k, held in registers for all queries; B = 16 queries x 32 k,
+// loaded directly (k contiguous); D lands as 4 consecutive features of one
+// query per lane.
+constexpr int kNope = 256;   // q_nope width per head
+constexpr int kVdim = 256;   // value width per head (output of the projection)
+constexpr int kAbsorbRows = 64;  // queries per work-group (grid z spreads the rest)
+
+// grid (8 slices of 64 latent dimensions, 64 heads), 256 threads: wave w
+// computes latent dimensions n0 + 16w .. n0 + 16w + 15.  W_UK[h] rows are
+// latent-contiguous, so the slice is staged in LDS (row stride 144 B) and
+// read transposed with ds_read_b64_tr_b16.
+__global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
+    constexpr int RS = 144;
+    __shared__ __attribute__((aligned(16))) uint8_t wl[kNope * RS];
+    const int h = blockIdx.y, n0 = 64 * blockIdx.x;
+    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+    const int m_begin = kAbsorbRows * blockIdx.z;
+    const int m_end = m_begin + kAbsorbRows < a.n_q ? m_begin + kAbsorbRows : a.n_q;
+    // this lane's query row of a 16-query block, k = 32 ks + 8 g .. + 7
+    auto load_q = [&](int m0, bf16x8 (&bq)[kNope / 32]) {
+        const int m = m0 + n;
+        const uint16_t *qn = a.q_nope + ((size_t)(m < m_end ? m : m_begin) * kHeads + h) * kNope + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kNope / 32; ks++) bq[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qn + 32 * ks));
+    };
+    bf16x8 bq[kNope / 32];
+    load_q(m_begin, bq);                      // in flight while the weights are staged
+    {
+        const uint8_t *W = reinterpret_cast<const uint8_t *>(a.w_uk + (size_t)h * kNope * kLatent + n0);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int e = threadIdx.x + 256 * i, r = e >> 3, pc = e & 7;
+            *(u32x4 *)(wl + r * RS + 16 * pc) = *(const u32x4 *)(W + (size_t)r * kLatent * 2 + 16 * pc);
+        }
+    }
+    __syncthreads();
+    bf16x8 wa[kNope / 32];
+    {
+        const int r_in = n >> 2, c_in = n & 3;
+#pragma unroll
+        for (int ks = 0; ks < kNope / 32; ks++) {
+            const uint8_t *p1 = wl + (32 * ks + 8 * g + r_in) * RS + (16 * w + 4 * c_in) * 2;
+            const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
+            const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1 + 4 * RS));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 tv = {t1[0], t1[1], t1[2], t1[3], t2[0], t2[1], t2[2], t2[3]};
+            wa[ks] = __builtin_bit_cast(bf16x8, tv);
+        }
+    }
+    const int D = kLatent + a.d_rope;
+    auto block = [&](int m0, const bf16x8 (&b)[kNope / 32]) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kNope / 32; ks++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b[ks], acc, 0, 0, 0);
+        const int m = m0 + n;
+        if (m < m_end) {
+            const uint32_t lo = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
+            const uint32_t hi = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
+            uint16_t *dst = a.q_abs + ((size_t)m * kHeads + h) * D + n0 + 16 * w + 4 * g;
+            *(uint2 *)dst = make_uint2(lo, hi);
+        }
+    };
+    // two query blocks per trip, each one's operands loaded a block ahead
+    bf16x8 bq2[kNope / 32];
+    for (int m0 = m_begin; m0 < m_end; m0 += 32) {
+        if (m0 + 16 < m_end) load_q(m0 + 16, bq2);
+        block(m0, bq);
+        if (m0 + 16 >= m_end) break;
+        if (m0 + 32 < m_end) load_q(m0 + 32, bq);
+        block(m0 + 16, bq2);
+    }
+    // the RoPE part, appended unchanged
+    if (blockIdx.x == 0 && a.d_rope > 0) {
+        for (int e = threadIdx.x; e < (m_end - m_begin) * (a.d_rope / 8); e += 256) {
+            const int m = m_begin + e / (a.d_rope / 8), pc = e % (a.d_rope / 8);
+            *(u32x4 *)(a.q_abs + ((size_t)m * kHeads + h) * D + kLatent + 8 * pc) =
+                *(const u32x4 *)(a.q_rope + ((size_t)m * kHeads + h) * a.d_rope + 8 * pc);
+        }
+    }
+}
+
+// grid (4 slices of 64 value dimensions, 64 heads, query chunks of
+// kAbsorbRows), 256 threads: wave w computes value dimensions i0 + 16w ..
+// i0 + 16w + 15; W_UV[h] rows are k-contiguous and go to registers directly.
+// o (fp32) enters the MFMA as bf16 hi + lo (the truncated value and the
+// rounded remainder, ~16 bits).
+__global__ __launch_bounds__(256) void k_project(AbsorbArgs a) {
+    const int h = blockIdx.y, i0 = 64 * blockIdx.x;
+    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+    const int m_begin = kAbsorbRows * blockIdx.z;
+    const int m_end = m_begin + kAbsorbRows < a.n_q ? m_begin + kAbsorbRows : a.n_q;
+    bf16x8 wa[kLatent / 32];
+    {
+        const uint16_t *W = a.w_uv + ((size_t)h * kVdim + i0 + 16 * w + n) * kLatent + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kLatent / 32; ks++) wa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(W + 32 * ks));
+    }
+    for (int m0 = m_begin; m0 < m_end; m0 += 16) {
+        const int m = m0 + n;
+        const float *op = a.o + ((size_t)(m < m_end ? m : m_begin) * kHeads + h) * kLatent + 8 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kLatent / 32; ks++) {
+            f32x4 x0 = *(const f32x4 *)(op + 32 * ks), x1 = *(const f32x4 *)(op + 32 * ks + 4);
+            if (m >= m_end) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 bh, bl;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float v = j < 4 ? x0[j] : x1[j - 4];
+                const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+                bh[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+                bl[j] = __builtin_bit_cast(__bf16, bf16_rne(v - __uint_as_float(hb)));
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], bl, acc, 0, 0, 0);
+        }
+        if (m < m_end) *(f32x4 *)(a.ctx + ((size_t)m * kHeads + h) * kVdim + i0 + 16 * w + 4 * g) = acc;
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
     const size_t words = bytes / 4;
@@ -1397,6 +1525,19 @@ hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st) {
     const int64_t pools = (a.max_new + 3) / 4;
     const unsigned gx = (unsigned)((pools + 3) / 4 > 0 ? (pools + 3) / 4 : 1);
     hipLaunchKernelGGL(k_pool_append, dim3(gx, a.n_seq), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+}  // namespace dsa
+
+namespace dsa {
+hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_absorb, dim3(kLatent / 64, kHeads, (a.n_q + kAbsorbRows - 1) / kAbsorbRows), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+}
+hipError_t launch_project(const AbsorbArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_project, dim3(kVdim / 64, kHeads, (a.n_q + kAbsorbRows - 1) / kAbsorbRows), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
 }
 }  // namespace dsa

@@ -202,6 +202,27 @@ int dsa_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new, i
                     dsa_bf16 *rolling, dsa_bf16 *pool_keys, int64_t pool_stride,
                     const float *pos_emb, hipStream_t stream);
 
+/* 6. Absorption GEMMs on either side of the attention ("GLM 5.2 in pure C",
+ * "Attention: Multi head Latent Attention With a Tiny KV Cache";
+ * TensorSharp2 table "The block": the per-head K/V decompression folded
+ * into the query and the output).  64 heads.
+ *   q_abs[m][h][n] = bf16( sum_{k<256} q_nope[m][h][k] * w_uk[h][k][n] )   n < 512
+ *   q_abs[m][h][512 + r] = q_rope[m][h][r]                                 r < d_rope
+ * fp32 accumulation, rounded to nearest even; the result is the absorbed
+ * query that dsa_mla_attend and dsa_decode_step take.
+ *   q_nope [n_q][64][256] bf16, q_rope [n_q][64][d_rope] bf16 (NULL if
+ *   d_rope is 0), w_uk [64][256][512] bf16 (the model's key up-projection
+ *   rows), q_abs [n_q][64][512 + d_rope] bf16.  d_rope is 0 or 64. */
+int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const dsa_bf16 *q_rope,
+                     const dsa_bf16 *w_uk, dsa_bf16 *q_abs, hipStream_t stream);
+
+/*   ctx[m][h][i] = sum_{j<512} o[m][h][j] * w_uv[h][i][j]                  i < 256
+ * o [n_q][64][512] fp32 (the attention output), w_uv [64][256][512] bf16
+ * (the model's value up-projection rows), ctx [n_q][64][256] fp32.  o
+ * enters the bf16 MFMA as two halves (truncated value + rounded
+ * remainder); |error| <= 2^-14 * sum_j |o_j w_ij|. */
+int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float *ctx, hipStream_t stream);
+
 /* Instrumentation for benchmarks.  With events set (n_events > 0), each
  * dsa_decode_step call on this thread records events[0] on its stream before
  * its first kernel and events[i + 1] after its i-th kernel (as many as fit),
