@@ -57,6 +57,24 @@ static double bf16_value(uint16_t bits)
     return (double)f;
 }
 
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double f16_value(uint16_t bits)
+{
+    const int e = (bits >> 10) & 31;
+    const int f = bits & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);                 /* zero and subnormals */
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return (bits & 0x8000u) ? -v : v;
+}
+
+/* An indexer element: bf16 bits, or IEEE f16 bits when f16 is set. */
+static double idx_value(uint16_t bits, int32_t f16)
+{
+    return f16 ? f16_value(bits) : bf16_value(bits);
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
@@ -76,12 +94,14 @@ int oracle_max_threads(void)
  * for r < rows(q) = q_nvis[q] / kpool.  Rows are tokens (kpool = 1) or
  * complete pools of kpool tokens ([WA] "k-pool flavour": one compressed
  * 128-wide key per pool).  Entries of s at r >= rows(q) are left untouched.
+ * qi and K hold bf16, or IEEE f16 when idx_f16 is set ([TS] "The
+ * sparse-attention path": the indexer key cache is F16).
  */
 int oracle_index_scores(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
                         int32_t kpool, int32_t n_idx_heads, int32_t d_idx,
                         const uint16_t *idx_q, const float *idx_w,
                         const uint16_t *idx_k, int64_t key_seq_stride,
-                        float *scores, int64_t score_ld)
+                        float *scores, int64_t score_ld, int32_t idx_f16)
 {
     for (int32_t q = 0; q < n_q; q++) {
         const int64_t rows = q_nvis[q] / kpool;
@@ -96,7 +116,7 @@ int oracle_index_scores(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis
             for (int32_t h = 0; h < n_idx_heads; h++) {
                 double dot = 0.0;
                 for (int32_t d = 0; d < d_idx; d++)
-                    dot += bf16_value(qi[h * d_idx + d]) * bf16_value(k[d]);
+                    dot += idx_value(qi[h * d_idx + d], idx_f16) * idx_value(k[d], idx_f16);
                 if (dot > 0.0)
                     acc += (double)w[h] * dot;
             }
@@ -261,7 +281,7 @@ int oracle_decode_step(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
                        const uint16_t *idx_k, int64_t key_seq_stride,
                        const uint16_t *q, const uint16_t *cache, int64_t cache_seq_stride,
                        int32_t *sel, int32_t sel_ld, int32_t *sel_count,
-                       float *out, float *lse)
+                       float *out, float *lse, int32_t idx_f16)
 {
     int64_t max_rows = 1;
     for (int32_t i = 0; i < n_q; i++)
@@ -269,7 +289,7 @@ int oracle_decode_step(int32_t n_q, const int32_t *q_seq, const int32_t *q_nvis,
     float *scores = (float *)malloc((size_t)n_q * (size_t)max_rows * sizeof *scores);
     if (!scores) return -2;
     int rc = oracle_index_scores(n_q, q_seq, q_nvis, kpool, n_idx_heads, d_idx,
-                                 idx_q, idx_w, idx_k, key_seq_stride, scores, max_rows);
+                                 idx_q, idx_w, idx_k, key_seq_stride, scores, max_rows, idx_f16);
     if (rc == 0)
         rc = oracle_topk(n_q, q_nvis, kpool, top_k, scores, max_rows, sel, sel_ld, sel_count);
     if (rc == 0)
@@ -420,6 +440,114 @@ int oracle_project_output(int32_t n_q, int32_t n_heads, int32_t d_latent, int32_
                 dst[i] = (float)acc;
             }
         }
+    }
+    return 0;
+}
+
+/*
+ * Indexer input preparation ([TS] "The sparse-attention path": once the
+ * context passes top_k the indexer applies rope and then a Walsh-Hadamard
+ * rotation to its queries and keys before scoring; the rotation is
+ * orthonormal and its own inverse, so it cancels in exact arithmetic, but the
+ * indexer key cache is F16 and rotating before the rounding spreads the
+ * rounding error evenly over the 128 dimensions.  [TS] "The block": RoPE
+ * NORM, base 8e6, no YaRN, on a 64-wide rope slice).
+ *
+ * For one d_idx-wide vector x at position p, in double:
+ *   rope:     for j < d_rope / 2 the pair (x[o + 2j], x[o + 2j + 1]),
+ *             o = d_idx - d_rope, turns by the angle p * base^(-2j / d_rope):
+ *                 (a, b) -> (a cos t - b sin t, a sin t + b cos t)
+ *   rotation: y[i] = d_idx^(-1/2) * sum_j (-1)^popcount(i & j) * x[j]
+ * Readings: the rope slice is the tail of the head, as in the attention
+ * query and cache row where the rope part follows the NoPE part; NORM turns
+ * adjacent pairs in place; the rotation is the Sylvester-ordered Hadamard
+ * matrix, scaled to be orthonormal.  d_idx is a power of two.
+ */
+void oracle_index_rotate(int32_t d_idx, int32_t d_rope, double base, int64_t pos,
+                         const double *x, double *y)
+{
+    double r[1024];
+    memcpy(r, x, (size_t)d_idx * sizeof *r);
+    const int32_t o = d_idx - d_rope;
+    for (int32_t j = 0; j < d_rope / 2; j++) {
+        const double t = (double)pos * pow(base, -2.0 * j / d_rope);
+        const double a = x[o + 2 * j], b = x[o + 2 * j + 1];
+        r[o + 2 * j] = a * cos(t) - b * sin(t);
+        r[o + 2 * j + 1] = a * sin(t) + b * cos(t);
+    }
+    const double norm = 1.0 / sqrt((double)d_idx);
+    for (int32_t i = 0; i < d_idx; i++) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < d_idx; j++)
+            acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -r[j] : r[j];
+        y[i] = acc * norm;
+    }
+}
+
+/* Nearest IEEE f16 (ties to even) of a double, subnormals and overflow to
+ * infinity included. */
+static uint16_t f16_from_double(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (isnan(a)) return 0x7e00u;
+    if (a < ldexp(1.0, -14))                      /* quantum 2^-24; may round up to 2^-14 */
+        return sign | (uint16_t)rint(ldexp(a, 24));
+    int e;
+    double m = frexp(a, &e);                      /* a = m * 2^e, m in [0.5, 1) */
+    double r = rint(ldexp(m, 11));                /* 11 significant bits, ties to even */
+    if (r == 2048.0) { r = 1024.0; e += 1; }
+    const int E = e - 1 + 15;
+    if (E >= 31) return sign | 0x7c00u;
+    return sign | (uint16_t)(E << 10) | (uint16_t)((int)r - 1024);
+}
+
+/* Rounds n doubles to bf16 or (f16 set) IEEE f16 bits. */
+void oracle_round16(int64_t n, const double *v, uint16_t *out, int32_t f16)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = f16 ? f16_from_double(v[i]) : bf16_from_double(v[i]);
+}
+
+/*
+ * Prepares a step's indexer inputs from their float projections:
+ *  - query head h of query q sits at position q_nvis[q] - 1 (the query's own
+ *    token is the last one it sees) and goes to q_out[q][h];
+ *  - new key i sits at position k_pos[i] of sequence k_seq[i] (i when k_seq
+ *    is NULL) and is appended at that row of the key cache,
+ *    k_cache[seq][pos]; a key whose sequence or position lies outside
+ *    [0, n_seq) x [0, key_seq_stride) is not written.
+ * Each vector is rotated as above and rounded to bf16, or f16 when idx_f16.
+ *   q_in [n_q][n_idx_heads][d_idx], k_in [n_new][d_idx] float.
+ */
+int oracle_index_prepare(int32_t n_q, int32_t n_idx_heads, int32_t d_idx, int32_t d_rope, double base,
+                         const int32_t *q_nvis, const float *q_in, uint16_t *q_out,
+                         int32_t n_new, int32_t n_seq, const int32_t *k_seq, const int32_t *k_pos,
+                         const float *k_in, uint16_t *k_cache, int64_t key_seq_stride, int32_t idx_f16)
+{
+    if (d_idx > 1024 || (d_idx & (d_idx - 1)) || d_rope < 0 || d_rope > d_idx || (d_rope & 1)) return -1;
+    const int64_t n_vec = (int64_t)n_q * n_idx_heads;
+    #pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < n_vec + n_new; v++) {
+        double x[1024], y[1024];
+        const float *src;
+        uint16_t *dst;
+        int64_t pos;
+        if (v < n_vec) {
+            pos = (int64_t)q_nvis[v / n_idx_heads] - 1;
+            src = q_in + v * d_idx;
+            dst = q_out + v * d_idx;
+        } else {
+            const int64_t i = v - n_vec;
+            const int64_t seq = k_seq ? k_seq[i] : i;
+            pos = k_pos[i];
+            if (seq < 0 || seq >= n_seq || pos < 0 || pos >= key_seq_stride) continue;
+            src = k_in + i * d_idx;
+            dst = k_cache + (seq * key_seq_stride + pos) * d_idx;
+        }
+        for (int32_t d = 0; d < d_idx; d++) x[d] = (double)src[d];
+        oracle_index_rotate(d_idx, d_rope, base, pos, x, y);
+        oracle_round16(d_idx, y, dst, idx_f16);
     }
     return 0;
 }

@@ -33,15 +33,21 @@ def load(path: str):
     L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-    L.oracle_index_scores.argtypes = [i32, P, P, i32, i32, i32, P, P, P, i64, P, i64]
+    f64 = ctypes.c_double
+    L.oracle_index_scores.argtypes = [i32, P, P, i32, i32, i32, P, P, P, i64, P, i64, i32]
     L.oracle_topk.argtypes = [i32, P, i32, i32, P, i64, P, i32, P]
     L.oracle_mla_attend.argtypes = [i32, P, i32, i32, i32, f32, P, P, i64, P, i32, P, P, P]
     L.oracle_decode_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f32, i32, i32,
-                                     P, P, P, i64, P, P, i64, P, i32, P, P, P]
+                                     P, P, P, i64, P, P, i64, P, i32, P, P, P, i32]
     L.oracle_max_threads.argtypes = []
     L.oracle_pool_append.argtypes = [i32, P, P, P, i64, i32, P, P, i64, P]
     L.oracle_absorb_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
     L.oracle_project_output.argtypes = [i32, i32, i32, i32, P, P, P]
+    L.oracle_index_rotate.argtypes = [i32, i32, f64, i64, P, P]
+    L.oracle_index_rotate.restype = None
+    L.oracle_round16.argtypes = [i64, P, P, i32]
+    L.oracle_round16.restype = None
+    L.oracle_index_prepare.argtypes = [i32, i32, i32, i32, f64, P, P, P, i32, i32, P, P, P, P, i64, i32]
     for f in (L.oracle_index_scores, L.oracle_topk, L.oracle_mla_attend,
               L.oracle_decode_step, L.oracle_max_threads):
         f.restype = ctypes.c_int
@@ -70,11 +76,13 @@ def max_threads(L=None) -> int:
     return int((L or lib()).oracle_max_threads())
 
 
-def index_scores(q_seq, q_nvis, kpool, idx_q, idx_w, idx_k, score_ld=None, fill=np.nan, L=None):
+def index_scores(q_seq, q_nvis, kpool, idx_q, idx_w, idx_k, score_ld=None, fill=np.nan, L=None,
+                 f16=False):
     """Scores [n_q, score_ld] float32; entries past rows(q) hold ``fill``.
 
     idx_q: uint16 [n_q, HI, DI]; idx_w: float32 [n_q, HI];
-    idx_k: uint16 [n_seq, key_rows, DI]."""
+    idx_k: uint16 [n_seq, key_rows, DI]; 16-bit elements are bf16, or IEEE
+    f16 when ``f16``."""
     q_seq, q_nvis = _c(q_seq, np.int32), _c(q_nvis, np.int32)
     idx_q, idx_w, idx_k = _c(idx_q, np.uint16), _c(idx_w, np.float32), _c(idx_k, np.uint16)
     n_q, HI, DI = idx_q.shape
@@ -82,7 +90,7 @@ def index_scores(q_seq, q_nvis, kpool, idx_q, idx_w, idx_k, score_ld=None, fill=
         score_ld = max(1, int(q_nvis.max()) // kpool)
     out = np.full((n_q, score_ld), fill, dtype=np.float32)
     rc = (L or lib()).oracle_index_scores(n_q, _p(q_seq), _p(q_nvis), kpool, HI, DI, _p(idx_q),
-                                   _p(idx_w), _p(idx_k), idx_k.shape[1], _p(out), score_ld)
+                                   _p(idx_w), _p(idx_k), idx_k.shape[1], _p(out), score_ld, int(f16))
     assert rc == 0
     return out
 
@@ -122,7 +130,8 @@ def mla_attend(q_seq, d_latent, d_rope, scale, q, cache, sel, sel_count, want_ls
 
 
 def decode_step(geom, q_seq, q_nvis, idx_q, idx_w, idx_k, q, cache, sel_ld=None, L=None):
-    """Full step for every query.  Returns (sel, sel_count, out, lse)."""
+    """Full step for every query.  Returns (sel, sel_count, out, lse).  The
+    indexer elements are f16 when ``geom.get("idx_f16")``, else bf16."""
     q_seq, q_nvis = _c(q_seq, np.int32), _c(q_nvis, np.int32)
     idx_q, idx_w, idx_k = _c(idx_q, np.uint16), _c(idx_w, np.float32), _c(idx_k, np.uint16)
     q, cache = _c(q, np.uint16), _c(cache, np.uint16)
@@ -138,7 +147,8 @@ def decode_step(geom, q_seq, q_nvis, idx_q, idx_w, idx_k, q, cache, sel_ld=None,
                                   geom["d_latent"], geom["d_rope"], float(geom["softmax_scale"]),
                                   idx_q.shape[1], idx_q.shape[2], _p(idx_q), _p(idx_w),
                                   _p(idx_k), idx_k.shape[1], _p(q), _p(cache), cache.shape[1],
-                                  _p(sel), sel_ld, _p(cnt), _p(out), _p(lse))
+                                  _p(sel), sel_ld, _p(cnt), _p(out), _p(lse),
+                                  int(geom.get("idx_f16", 0)))
     assert rc == 0
     return sel, cnt, out, lse
 
@@ -192,3 +202,44 @@ def project_output(o, w_uv, L=None):
     rc = (L or lib()).oracle_project_output(n_q, H, dl, dv, _p(o), _p(w_uv), _p(out))
     assert rc == 0
     return out
+
+
+ROPE_BASE = 8.0e6
+
+
+def index_rotate(x, pos, d_rope, base=ROPE_BASE, L=None):
+    """Rope then orthonormal Walsh-Hadamard rotation of one vector, in double
+    and unrounded.  x: float64 [d_idx]."""
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    (L or lib()).oracle_index_rotate(x.shape[0], int(d_rope), float(base), int(pos), _p(x), _p(y))
+    return y
+
+
+def round16(v, f16, L=None):
+    """Nearest bf16 (or IEEE f16) bits of float64 values, ties to even."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    (L or lib()).oracle_round16(v.size, _p(v), _p(out), int(f16))
+    return out
+
+
+def index_prepare(q_nvis, q_in, k_seq, k_pos, k_in, k_cache, d_rope, f16, base=ROPE_BASE, L=None):
+    """Indexer queries (returned, uint16 [n_q, HI, DI]) and keys (appended in
+    place to ``k_cache`` uint16 [n_seq, stride, DI], which is returned too).
+
+    q_nvis int [n_q]; q_in float32 [n_q, HI, DI]; k_seq int [n_new] or None;
+    k_pos int [n_new]; k_in float32 [n_new, DI]."""
+    q_nvis, q_in = _c(q_nvis, np.int32), _c(q_in, np.float32)
+    k_pos, k_in = _c(k_pos, np.int32), _c(k_in, np.float32)
+    k_seq = None if k_seq is None else _c(k_seq, np.int32)
+    assert k_cache.dtype == np.uint16 and k_cache.flags.c_contiguous
+    n_q, HI, DI = q_in.shape
+    n_new = k_pos.shape[0]
+    assert k_in.shape == (n_new, DI) and k_cache.shape[2] == DI
+    q_out = np.empty((n_q, HI, DI), np.uint16)
+    rc = (L or lib()).oracle_index_prepare(n_q, HI, DI, int(d_rope), float(base), _p(q_nvis), _p(q_in),
+                                           _p(q_out), n_new, k_cache.shape[0], _p(k_seq), _p(k_pos),
+                                           _p(k_in), _p(k_cache), k_cache.shape[1], int(f16))
+    assert rc == 0
+    return q_out, k_cache

@@ -550,4 +550,155 @@ def pin_absorbed_attention_is_explicit_mla(L):
             assert np.allclose(ctx[m, h], want, rtol=2e-3, atol=2e-3 * np.abs(want).max())
 
 
+# ---------------------------------------------------------------- indexer input preparation
+BASE = 8.0e6          # RoPE base of the pages' model table
+
+
+def _sylvester():
+    """Orthonormal Walsh-Hadamard matrix from scipy (Sylvester order)."""
+    import scipy.linalg
+    return scipy.linalg.hadamard(DI).astype(np.float64) / math.sqrt(DI)
+
+
+def pin_prep_rotation_is_library_hadamard(L):
+    """Without rope (or at position 0, where rope turns by zero) the rotation
+    is scipy's Sylvester Hadamard matrix scaled by 1/sqrt(128)."""
+    Hm = _sylvester()
+    rng = np.random.default_rng(31)
+    for _ in range(3):
+        x = rng.standard_normal(DI)
+        assert np.allclose(O.index_rotate(x, 777, 0, L=L), Hm @ x, rtol=0, atol=1e-12)
+        assert np.allclose(O.index_rotate(x, 0, 64, L=L), Hm @ x, rtol=0, atol=1e-12)
+    e0 = np.zeros(DI)
+    e0[0] = 1.0
+    assert np.allclose(O.index_rotate(e0, 5, 0, L=L), np.full(DI, 1 / math.sqrt(DI)), atol=1e-15)
+
+
+def pin_prep_rotation_orthonormal_involution(L):
+    """The Hadamard rotation is orthonormal and its own inverse; with rope at
+    any position the map still preserves the norm (rope is a rotation)."""
+    rng = np.random.default_rng(32)
+    for pos in (1, 4097, 1048575):
+        x = rng.standard_normal(DI) * 3
+        y = O.index_rotate(x, 0, 0, L=L)
+        assert np.allclose(O.index_rotate(y, 0, 0, L=L), x, atol=1e-12)
+        z = O.index_rotate(x, pos, 64, L=L)
+        assert abs(np.linalg.norm(z) - np.linalg.norm(x)) < 1e-12 * np.linalg.norm(x)
+
+
+def pin_prep_rope_pairs_and_frequencies(L):
+    """Undoing the Hadamard rotation (scipy's matrix, its own inverse) leaves
+    the rope alone: the first 64 dimensions are untouched at any position;
+    the unit vector on dimension 64+2j stays in the pair (64+2j, 65+2j) and
+    turns counter-clockwise by p * base^(-2j/64).  Pair 0 turns by exactly p
+    radians; the angles at p = 1 form a geometric series of ratio
+    base^(-1/32)."""
+    Hm = _sylvester()
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal(DI)
+    for pos in (1, 3, 131071):
+        r = Hm @ O.index_rotate(x, pos, 64, L=L)
+        assert np.allclose(r[:64], x[:64], atol=1e-12)
+    ang = []
+    for j in range(32):
+        e = np.zeros(DI)
+        e[64 + 2 * j] = 1.0
+        r = Hm @ O.index_rotate(e, 1, 64, L=L)
+        rest = np.delete(r, [64 + 2 * j, 65 + 2 * j])
+        assert np.abs(rest).max() < 1e-12, j
+        ang.append(math.atan2(r[65 + 2 * j], r[64 + 2 * j]))
+    ang = np.array(ang)
+    assert abs(ang[0] - 1.0) < 1e-12
+    assert np.allclose(ang[1:] / ang[:-1], BASE ** (-1.0 / 32), rtol=1e-9)
+    assert abs(ang[31] - BASE ** (-62.0 / 64)) < 1e-15
+    e = np.zeros(DI)
+    e[64] = 1.0
+    r = Hm @ O.index_rotate(e, 2, 64, L=L)
+    assert abs(r[64] - math.cos(2.0)) < 1e-12 and abs(r[65] - math.sin(2.0)) < 1e-12
+
+
+def pin_prep_relative_position(L):
+    """Rope makes the score depend on the distance only, and the rotation
+    applied to both sides cancels: q(p).k(s) == q(p+d).k(s+d), and equals
+    q.k when p == s."""
+    rng = np.random.default_rng(34)
+    q, k = rng.standard_normal(DI), rng.standard_normal(DI)
+    for p, s_, d in ((10, 3, 1000), (0, 70000, 12345)):
+        a = O.index_rotate(q, p, 64, L=L) @ O.index_rotate(k, s_, 64, L=L)
+        b = O.index_rotate(q, p + d, 64, L=L) @ O.index_rotate(k, s_ + d, 64, L=L)
+        assert abs(a - b) < 1e-9
+    same = O.index_rotate(q, 4242, 64, L=L) @ O.index_rotate(k, 4242, 64, L=L)
+    assert abs(same - q @ k) < 1e-10
+
+
+def pin_prep_rounding(L):
+    """f16 rounding equals numpy's float64 -> float16 conversion (nearest,
+    ties to even, subnormals, overflow to infinity); bf16 ties go to even."""
+    rng = np.random.default_rng(35)
+    v = np.concatenate([
+        rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, -70000.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+         2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -(1 + 2.0 ** -11)]])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.round16(v, True, L=L), ref)
+    b = O.round16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -20]),
+                  False, L=L)
+    assert fl(b).tolist() == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+
+
+def pin_prep_f16_scores(L):
+    """Scores over f16 inputs equal a float64 evaluation of numpy's decoding
+    of the same f16 bits (normal, subnormal and integer values)."""
+    rng = np.random.default_rng(36)
+    qi = (rng.standard_normal((2, HI, DI)) * 4).astype(np.float16)
+    K = (rng.standard_normal((1, 80, DI)) * 2.0 ** rng.integers(-20, 4, (1, 80, 1))).astype(np.float16)
+    w = rng.standard_normal((2, HI)).astype(np.float32)
+    s = O.index_scores([0, 0], [80, 41], 1, qi.view(np.uint16), w, K.view(np.uint16), L=L, f16=True)
+    for j, rows in enumerate((80, 41)):
+        ref = np.maximum(K[0, :rows].astype(np.float64) @ qi[j].astype(np.float64).T, 0) @ w[j].astype(np.float64)
+        assert np.allclose(s[j, :rows], ref, rtol=1e-6, atol=1e-30)
+    # integer f16 inputs: exact, equal to the int64 brute force
+    qz = rng.integers(-8, 9, size=(1, HI, DI))
+    Kz = rng.integers(-8, 9, size=(1, 50, DI))
+    wz = rng.integers(-2, 5, size=(1, HI))
+    s = O.index_scores([0], [50], 1, qz.astype(np.float16).view(np.uint16), wz.astype(np.float32),
+                       Kz.astype(np.float16).view(np.uint16), L=L, f16=True)
+    assert np.array_equal(s[0], brute_scores(qz[0], wz[0], Kz[0], 50).astype(np.float32))
+
+
+def pin_prep_positions_and_rows(L):
+    """A query at n_vis = p + 1 sits at position p and a key appended at p
+    sits at p: with both equal to one vector x whose energy is on rope pair
+    0, q.k returns |x|^2 up to the 16-bit rounding (a position off by one
+    turns pair 0 by a radian).  A query with n_vis = 1 is the plain
+    rotation.  Keys land at row (seq, pos); a key whose sequence or position
+    is out of range writes nothing; every other row is untouched."""
+    Hm = _sylvester()
+    rng = np.random.default_rng(37)
+    n_seq, stride = 3, 40
+    for f16 in (False, True):
+        x = rng.standard_normal(DI) * 0.05
+        x[64], x[65] = 6.0, 8.0
+        q_in = np.stack([np.tile(x, (HI, 1)), rng.standard_normal((HI, DI))]).astype(np.float32)
+        q_nvis = np.array([30, 1])
+        k_pos = np.array([29, 0, 39, 40, -1, 5])
+        k_seq = np.array([1, 0, 2, 0, 1, -1])
+        k_in = np.stack([x] + [rng.standard_normal(DI) for _ in range(5)]).astype(np.float32)
+        cache = np.full((n_seq, stride, DI), 0x1234, np.uint16)
+        qo, cache = O.index_prepare(q_nvis, q_in, k_seq, k_pos, k_in, cache, 64, f16, L=L)
+        dec = (lambda b: b.view(np.float16).astype(np.float64)) if f16 else fl
+        dot = dec(qo[0, 5]) @ dec(cache[1, 29])
+        assert abs(dot - x.astype(np.float32).astype(np.float64) @ x.astype(np.float32)) < 0.05 * 100 * 2 ** -6, dot
+        plain = Hm @ q_in[1, 3].astype(np.float64)
+        assert np.allclose(dec(qo[1, 3]), plain, rtol=2 ** -7, atol=1e-30)
+        written = {(1, 29), (0, 0), (2, 39)}
+        for s_ in range(n_seq):
+            for r in range(stride):
+                if (s_, r) not in written:
+                    assert (cache[s_, r] == 0x1234).all(), (f16, s_, r)
+        k0 = dec(cache[0, 0])
+        assert np.allclose(k0, Hm @ k_in[1].astype(np.float64), rtol=2 ** -7, atol=1e-30)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -14,8 +14,8 @@ from oracle import oracle as O
 MUTANTS = [
     ("relu_dropped", "if (dot > 0.0)\n                    acc +=", "if (1)\n                    acc +="),
     ("relu_after_weight", "if (dot > 0.0)\n                    acc +=", "if ((double)w[h] * dot > 0.0)\n                    acc +="),
-    ("key_index_shifted", "bf16_value(k[d]);", "bf16_value(k[(d + 1) % d_idx]);"),
-    ("head_stride_wrong", "bf16_value(qi[h * d_idx + d])", "bf16_value(qi[h + d])"),
+    ("key_index_shifted", "idx_value(k[d], idx_f16);", "idx_value(k[(d + 1) % d_idx], idx_f16);"),
+    ("head_stride_wrong", "idx_value(qi[h * d_idx + d], idx_f16)", "idx_value(qi[h + d], idx_f16)"),
     ("rows_off_by_one", "const int64_t rows = q_nvis[q] / kpool;", "const int64_t rows = (q_nvis[q] - 1) / kpool;"),
     ("seq_ignored_in_scores", "const int64_t seq = q_seq ? q_seq[q] : q;", "const int64_t seq = 0;"),
     ("ties_to_higher_index", "return (a->r > b->r) - (a->r < b->r);", "return (a->r < b->r) - (a->r > b->r);"),
@@ -52,6 +52,22 @@ MUTANTS = [
     ("project_wrong_head_weight", "const uint16_t *W = w_uv + (int64_t)h * d_v * d_latent;", "const uint16_t *W = w_uv;"),
     ("project_half_the_latent", "for (int32_t j = 0; j < d_latent; j++)\n                    acc += (double)oh[j]",
      "for (int32_t j = 0; j < d_latent / 2; j++)\n                    acc += (double)oh[j]"),
+    ("f16_keys_read_as_bf16", "idx_value(k[d], idx_f16);", "idx_value(k[d], 0);"),
+    ("f16_decode_bias", "else v = ldexp((double)(1024 + f), e - 25);", "else v = ldexp((double)(1024 + f), e - 24);"),
+    ("prep_rotation_unscaled", "y[i] = acc * norm;", "y[i] = acc;"),
+    ("prep_hadamard_sign_pattern", "__builtin_popcount((unsigned)(i & j))", "__builtin_popcount((unsigned)(i | j))"),
+    ("prep_rope_on_head", "const int32_t o = d_idx - d_rope;", "const int32_t o = 0;"),
+    ("prep_rope_neox_pairs", "const double a = x[o + 2 * j], b = x[o + 2 * j + 1];",
+     "const double a = x[o + j], b = x[o + j + d_rope / 2];"),
+    ("prep_rope_not_a_rotation", "r[o + 2 * j] = a * cos(t) - b * sin(t);", "r[o + 2 * j] = a * cos(t) + b * sin(t);"),
+    ("prep_rope_clockwise", "r[o + 2 * j] = a * cos(t) - b * sin(t);\n        r[o + 2 * j + 1] = a * sin(t) + b * cos(t);",
+     "r[o + 2 * j] = a * cos(t) + b * sin(t);\n        r[o + 2 * j + 1] = -a * sin(t) + b * cos(t);"),
+    ("prep_rope_frequency_exponent", "pow(base, -2.0 * j / d_rope)", "pow(base, -2.0 * j / (d_rope - 2))"),
+    ("prep_query_position_off", "pos = (int64_t)q_nvis[v / n_idx_heads] - 1;", "pos = (int64_t)q_nvis[v / n_idx_heads];"),
+    ("prep_key_row_transposed", "dst = k_cache + (seq * key_seq_stride + pos) * d_idx;",
+     "dst = k_cache + (pos * n_seq + seq) * d_idx;"),
+    ("prep_f16_truncates", "double r = rint(ldexp(m, 11));", "double r = trunc(ldexp(m, 11));"),
+    ("prep_f16_subnormal_scale", "return sign | (uint16_t)rint(ldexp(a, 24));", "return sign | (uint16_t)rint(ldexp(a, 25));"),
 ]
 
 
