@@ -63,7 +63,7 @@ def score_kernel_hash() -> str:
     its template line to its closing brace."""
     import hashlib
     src = open(KERNEL_SRC).read()
-    i = src.index("template <bool STRIDE>\n__global__ __launch_bounds__(256) void k_score(Args a) {")
+    i = src.index("template <bool STRIDE, bool F16>\n__global__ __launch_bounds__(256) void k_score(Args a) {")
     j = src.index("\n}\n", i) + 3
     return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
 
@@ -122,6 +122,9 @@ def main() -> int:
                     help="time the k-pool key producer instead: one bulk append of 2^20 - 1 tokens")
     ap.add_argument("--absorb", action="store_true",
                     help="time the absorption GEMMs instead (absorb + project, 8 and 512 queries)")
+    ap.add_argument("--prepare", action="store_true",
+                    help="time the indexer input preparation (rope + Hadamard + rounding, key append) instead")
+    ap.add_argument("--f16", action="store_true", help="indexer queries and keys in f16 (prepare and decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (to scale byte counters)")
     args = ap.parse_args()
@@ -132,6 +135,8 @@ def main() -> int:
 
     if args.producer:
         return run_producer(args)
+    if args.prepare:
+        return run_prepare(args)
     if args.absorb:
         return run_absorb(args)
 
@@ -373,6 +378,106 @@ def run_absorb(args) -> int:
         el = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(8 / el, 1), "unit": "queries/s", "cores": O.max_threads(),
                                "kind": "oracle", "sample": f"one decode batch of 8 queries, {el:.2f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_prepare(args) -> int:
+    """Indexer input preparation: rope on the tail 64 dimensions, the
+    orthonormal Walsh-Hadamard rotation and rounding to the indexer's 16-bit
+    format, for the indexer queries of a step (32 heads x 128, float32 in) and
+    the keys it appends to the key cache.  Timed for a decode batch (8
+    queries, 8 keys) and a 512-token prefill chunk (512 queries, 512 keys);
+    the decode batch is the headline, the chunk is the bandwidth case."""
+    import torch
+    from deepseek_sparse_attention_amd import binding as B
+    from deepseek_sparse_attention_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    B.device_check()
+    geom = dict(I.GEOM_TOKEN, idx_f16=int(args.f16))
+    T = 131072
+
+    def timed(n_q, n_new, n_seq):
+        # decode: query i and key i belong to sequence i, at position T - 1;
+        # chunk: one sequence, queries and keys at positions T - n .. T - 1
+        q_in, k_in = I.indexer_projections(11, n_q, n_new)
+        dev = "cuda"
+        per = n_new // n_seq
+        q_seq = torch.arange(n_q, dtype=torch.int32, device=dev) % n_seq
+        q_nvis = (T - per + 1 + torch.arange(n_q, dtype=torch.int32, device=dev) // n_seq).to(torch.int32)
+        b = B.batch(q_seq, q_nvis, T, n_seq)
+        k_seq = torch.arange(n_new, dtype=torch.int32, device=dev) % n_seq
+        k_pos = (T - per + torch.arange(n_new, dtype=torch.int32, device=dev) // n_seq).to(torch.int32)
+        d_q, d_k = torch.from_numpy(q_in).to(dev), torch.from_numpy(k_in).to(dev)
+        q_out = torch.empty((n_q, 32, 128), dtype=torch.int16, device=dev)
+        cache = torch.zeros((n_seq, T, 128), dtype=torch.int16, device=dev)
+        for _ in range(args.warmup):
+            B.index_prepare(geom, b, d_q, q_out, k_seq, k_pos, d_k, cache, T)
+        torch.cuda.synchronize()
+        # the call takes less device time than its host-side launch: time it
+        # replayed from a captured graph of `per_graph` calls
+        per_graph = 50
+        graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+            for _ in range(per_graph):
+                B.index_prepare(geom, b, d_q, q_out, k_seq, k_pos, d_k, cache, T)
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // per_graph)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            graph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / (reps * per_graph)
+        nbytes = n_q * (32 * 128 * (4 + 2) + 4) + n_new * (128 * (4 + 2) + 8)
+        # reference at the same size: torch's float32 -> bfloat16 cast of the
+        # queries (the same bytes read and written per element), same timing
+        cast_out = torch.empty((n_q, 32, 128), dtype=torch.bfloat16, device=dev)
+        cgraph = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side), torch.cuda.graph(cgraph, stream=side):
+            for _ in range(per_graph):
+                cast_out.copy_(d_q)
+        torch.cuda.current_stream().wait_stream(side)
+        cgraph.replay()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            cgraph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        cast_us = ev[0].elapsed_time(ev[1]) * 1e3 / (reps * per_graph)
+        return {"queries": n_q, "keys": n_new, "us": round(us, 3), "bytes": nbytes,
+                "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "torch_cast_us": round(cast_us, 3), "torch_cast_bytes": n_q * 32 * 128 * 6}
+
+    dec, pre = timed(8, 8, 8), timed(512, 512, 1)
+    res = {
+        "metric": "indexer input preparation, decode batch of 8 queries + 8 appended keys per second",
+        "value": round(8 / (dec["us"] * 1e-6), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dec["us"] * 1e-3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "indexer rope + Hadamard + rounding to " + ("f16" if args.f16 else "bf16")
+                               + ", 32 heads x 128, keys appended at position 131071"},
+        "roofline": {"bound": "hbm", "kernel": "k_index_prep (512-token chunk)", "achieved": pre["GBps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pre["GBps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": pre["bytes"]},
+        "decode_8": dec, "prefill_512": pre,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        q_in, k_in = I.indexer_projections(11, 8, 8)
+        t0 = time.perf_counter()
+        O.index_prepare(np.full(8, T, np.int32), q_in, np.arange(8, dtype=np.int32), np.full(8, T - 1, np.int32),
+                        k_in, np.zeros((8, T, 128), np.uint16), 64, args.f16)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(8 / el, 1), "unit": "queries/s", "cores": O.max_threads(),
+                               "kind": "oracle", "sample": f"one decode batch of 8 queries + 8 keys, {el:.3f} s"}
     print(json.dumps(res), flush=True)
     return 0
 

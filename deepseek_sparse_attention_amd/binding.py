@@ -19,7 +19,7 @@ DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_DEVICE, DSA
 class Geometry(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("n_idx_heads", ctypes.c_int32), ("d_idx", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("kpool", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("kpool", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("idx_f16", ctypes.c_int32)]
 
 
 class Batch(ctypes.Structure):
@@ -28,8 +28,8 @@ class Batch(ctypes.Structure):
 
 
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
-           "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_status_str", "dsa_last_error", "dsa_device_check",
-           "dsa_set_timing_events")
+           "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_index_prepare",
+           "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events")
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -48,6 +48,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_pool_append": (ctypes.c_int, [i32, P, P, i32, P, i64, P, P, i64, P, P]),
         "dsa_absorb_query": (ctypes.c_int, [i32, i32, P, P, P, P, P]),
         "dsa_project_output": (ctypes.c_int, [i32, P, P, P, P]),
+        "dsa_index_prepare": (ctypes.c_int, [G, B, ctypes.c_double, P, P, i32, P, P, P, P, i64, P]),
         "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_device_check": (ctypes.c_int, []),
@@ -76,7 +77,7 @@ def _check(status: int, what: str) -> None:
 
 def geometry(geom: dict) -> Geometry:
     return Geometry(geom["n_heads"], geom["d_latent"], geom["d_rope"], geom["n_idx_heads"], geom["d_idx"],
-                    geom["top_k"], geom["kpool"], float(geom["softmax_scale"]))
+                    geom["top_k"], geom["kpool"], float(geom["softmax_scale"]), int(geom.get("idx_f16", 0)))
 
 
 def _ptr(t: torch.Tensor | None):
@@ -190,6 +191,30 @@ def project_output(o, w_uv, ctx, stream=None) -> None:
         if not t.is_cuda or not t.is_contiguous():
             raise TypeError("project_output takes contiguous cuda tensors")
     _check(_lib.dsa_project_output(n_q, _ptr(o), _ptr(w_uv), _ptr(ctx), _stream(stream)), "dsa_project_output")
+
+
+def index_prepare(geom: dict, b: Batch, q_in, q_out, k_seq, k_pos, k_in, idx_k, key_seq_stride: int,
+                  rope_base: float = 8.0e6, stream=None) -> None:
+    """Rope + Hadamard rotation + 16-bit rounding of indexer queries (q_in
+    float32 [n_q, 32, 128] -> q_out 16-bit, or both None) and of new keys
+    (k_in float32 [n_new, 128] at k_pos int32 [n_new] of k_seq int32 [n_new]
+    or None, written into idx_k 16-bit [n_seq, key_seq_stride, 128]).  The
+    16-bit format is the geometry's idx_f16."""
+    n_new = 0 if k_pos is None else int(k_pos.shape[0])
+    if q_in is not None and q_out is not None:     # one without the other is refused by the library
+        if q_in.dtype != torch.float32 or q_out.element_size() != 2 or tuple(q_in.shape) != tuple(q_out.shape):
+            raise TypeError("index_prepare: q_in float32 and q_out 16-bit of one shape")
+    if n_new:
+        if k_in.dtype != torch.float32 or tuple(k_in.shape) != (n_new, 128) or idx_k.element_size() != 2:
+            raise TypeError("index_prepare: k_in float32 [n_new, 128], idx_k 16-bit")
+        if k_pos.dtype != torch.int32 or (k_seq is not None and k_seq.dtype != torch.int32):
+            raise TypeError("index_prepare: k_pos and k_seq int32")
+    for t in (q_in, q_out, k_seq, k_pos, k_in, idx_k):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise TypeError("index_prepare takes contiguous cuda tensors")
+    _check(_lib.dsa_index_prepare(ctypes.byref(geometry(geom)), ctypes.byref(b), float(rope_base), _ptr(q_in),
+                                  _ptr(q_out), n_new, _ptr(k_seq), _ptr(k_pos), _ptr(k_in), _ptr(idx_k),
+                                  int(key_seq_stride), _stream(stream)), "dsa_index_prepare")
 
 
 def set_timing_events(events) -> None:

@@ -27,6 +27,7 @@ hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void
 hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
 hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st);
 hipError_t launch_project(const AbsorbArgs &a, hipStream_t st);
+hipError_t launch_index_prep(const PrepArgs &a, hipStream_t st);
 }  // namespace dsa
 
 namespace {
@@ -84,6 +85,8 @@ int check_geometry(const dsa_geometry *g) {
         return fail(DSA_ERR_UNSUPPORTED, "top_k must be in [1, 4096] and a multiple of kpool");
     if (!(std::isfinite(g->softmax_scale) && g->softmax_scale > 0.f))
         return fail(DSA_ERR_UNSUPPORTED, "softmax_scale must be finite and positive");
+    if (g->idx_f16 != 0 && g->idx_f16 != 1) return fail(DSA_ERR_UNSUPPORTED, "idx_f16 must be 0 or 1");
+    if (g->idx_f16 && g->kpool != 1) return fail(DSA_ERR_UNSUPPORTED, "f16 indexer inputs need kpool 1");
     return DSA_OK;
 }
 
@@ -131,6 +134,7 @@ dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &
     a.score_tile = p.score_tile;
     a.prefill = b->q_per_seq_hint >= 2 ? 1 : 0;
     a.pf_run = b->q_per_seq_hint;
+    a.idx_f16 = g->idx_f16;
     return a;
 }
 
@@ -416,6 +420,47 @@ int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float 
         a.w_uv = w_uv;
         a.ctx = ctx;
         return launched(dsa::launch_project(a, stream), "project");
+    });
+}
+
+int dsa_index_prepare(const dsa_geometry *g, const dsa_batch *b, double rope_base, const float *q_in,
+                      dsa_bf16 *q_out, int32_t n_new, const int32_t *k_seq, const int32_t *k_pos, const float *k_in,
+                      dsa_bf16 *idx_k, int64_t key_seq_stride, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        DSA_TRY(check_geometry(g));
+        if (g->kpool != 1) return fail(DSA_ERR_UNSUPPORTED, "indexer preparation is for kpool 1 only");
+        DSA_TRY(check_batch(b));
+        if (!(std::isfinite(rope_base) && rope_base > 1.0)) return fail(DSA_ERR_ARG, "rope_base must be finite and > 1");
+        if ((q_in == nullptr) != (q_out == nullptr)) return fail(DSA_ERR_ARG, "q_in and q_out go together");
+        if (q_in && (!aligned16(q_in) || !aligned16(q_out)))
+            return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");
+        if (n_new < 0) return fail(DSA_ERR_ARG, "n_new < 0");
+        if (n_new > 0) {
+            if (!k_pos || !k_in || !idx_k) return fail(DSA_ERR_ARG, "NULL key pointer");
+            if (!k_seq && n_new > b->n_seq) return fail(DSA_ERR_ARG, "k_seq NULL needs n_new <= n_seq");
+            if (key_seq_stride < 1) return fail(DSA_ERR_ARG, "key_seq_stride < 1");
+            if (!aligned16(k_pos) || !aligned16(k_in) || !aligned16(idx_k) || (k_seq && !aligned16(k_seq)))
+                return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");
+        }
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        dsa::PrepArgs a{};
+        a.n_q = q_in ? b->n_q : 0;
+        a.n_new = n_new;
+        a.n_seq = b->n_seq;
+        a.rope = g->d_rope == 64 ? 1 : 0;
+        a.f16 = g->idx_f16;
+        for (int i = 0; i < 8; i++) a.inv_freq[i] = std::pow(rope_base, -4.0 * i / 32.0);
+        a.freq_ratio = std::pow(rope_base, -1.0 / 32.0);
+        a.q_nvis = b->q_nvis;
+        a.q_in = q_in;
+        a.q_out = q_out;
+        a.k_seq = k_seq;
+        a.k_pos = k_pos;
+        a.k_in = k_in;
+        a.k_cache = idx_k;
+        a.key_stride = key_seq_stride;
+        return launched(dsa::launch_index_prep(a, stream), "index_prep");
     });
 }
 

@@ -40,6 +40,7 @@ struct Args {
     int32_t fused;        // 1: dense queries are not scored, histogram accumulated
     int32_t prefill;      // 1: queries come in runs of pf_run that share a sequence
     int32_t pf_run;       // queries per run (>= 2 when prefill)
+    int32_t idx_f16;      // indexer queries and keys are IEEE f16 (else bf16)
 };
 
 // Arguments of the k-pool key producer.
@@ -65,6 +66,23 @@ struct AbsorbArgs {
     const float *o;          // [n_q][64][512]
     const uint16_t *w_uv;    // [64][256][512]
     float *ctx;              // [n_q][64][256]
+};
+
+// Arguments of the indexer input preparation.
+struct PrepArgs {
+    int32_t n_q, n_new, n_seq;
+    int32_t rope;              // 1: rope on the tail 64 dimensions of every vector
+    int32_t f16;               // output format: 1 IEEE f16, 0 bf16
+    double inv_freq[8];        // base^(-4i/32): frequency of rope pair 4i
+    double freq_ratio;         // base^(-1/32): from pair j to pair j + 1
+    const int32_t *q_nvis;     // [n_q]; a query sits at position q_nvis - 1
+    const float *q_in;         // [n_q][32][128], or NULL with n_q = 0
+    uint16_t *q_out;           // [n_q][32][128]
+    const int32_t *k_seq;      // [n_new] or NULL: key i goes to sequence i
+    const int32_t *k_pos;      // [n_new] position = cache row
+    const float *k_in;         // [n_new][128]
+    uint16_t *k_cache;         // [n_seq][key_stride][128]
+    int64_t key_stride;
 };
 
 }  // namespace dsa

@@ -203,6 +203,19 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
 }
 
 // ---------------------------------------------------------------- scores
+// One 16x16x32 MFMA step of the indexer on 16-bit operands: bf16, or IEEE
+// f16 when F16 (the two formats of the indexer queries and key cache).
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_idx(bf16x8 a, bf16x8 b, f32x4 c) {
+    if constexpr (F16) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+}
+
 // grid (tiles, n_q), 256 threads.  Wave w of a work-group takes 64-row
 // steps t0 + 64 (w + 4 i).  Keys are read with fully coalesced 16-byte loads
 // (one wave instruction = 1 KiB = 4 rows), the next step's 16 KiB already in
@@ -215,7 +228,7 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
 // for k-step s.  D[head][row] lands as lane (g, n) holding heads 4g + r
 // (+16) of row n; the epilogue applies ReLU and the head weights and sums
 // the four lane groups.
-template <bool STRIDE>
+template <bool STRIDE, bool F16>
 __global__ __launch_bounds__(256) void k_score(Args a) {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(16))) uint8_t tiles[4][64 * 256];
@@ -282,8 +295,8 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], b, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], b, acc1, 0, 0, 0);
+                acc0 = mfma_idx<F16>(qa[0][s], b, acc0);
+                acc1 = mfma_idx<F16>(qa[1][s], b, acc1);
             }
             float x = 0.f;
 #pragma unroll
@@ -332,6 +345,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
 constexpr int kPfTile = 128;     // key rows per LDS tile
 constexpr int kPfRange = 4096;   // key rows per work-group
 
+template <bool F16>
 __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kPfTile * 256];
     __shared__ uint32_t lh[kPfQ][kHistBins / 2];
@@ -413,8 +427,8 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], bv, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], bv, acc1, 0, 0, 0);
+            acc0 = mfma_idx<F16>(qa[0][s], bv, acc0);
+            acc1 = mfma_idx<F16>(qa[1][s], bv, acc1);
         }
         float x = 0.f;
 #pragma unroll
@@ -1472,23 +1486,28 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
+template <bool F16>
+hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st) {
     if (a.prefill) {
         const unsigned ranges = (unsigned)((max_rows + kPfRange - 1) / kPfRange);
         const unsigned runs = (unsigned)((a.n_q + a.pf_run - 1) / a.pf_run);
         const unsigned per = (unsigned)((a.pf_run + kPfQ - 1) / kPfQ);
-        hipLaunchKernelGGL(k_score_prefill, dim3(ranges, runs * per), dim3(512), 0, st, a);
+        hipLaunchKernelGGL(k_score_prefill<F16>, dim3(ranges, runs * per), dim3(512), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // in prefill mode k_score only picks up queries outside their block's
     // sequence: one work-group per query, striding over the tiles
     if (a.prefill)
-        hipLaunchKernelGGL(k_score<true>, dim3(1, a.n_q), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_score<true, F16>), dim3(1, a.n_q), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_score<false>, dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q),
-                           dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_score<false, F16>),
+                           dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
+    return a.idx_f16 ? launch_score_fmt<true>(a, max_rows, st) : launch_score_fmt<false>(a, max_rows, st);
 }
 
 hipError_t launch_hist(const Args &a, hipStream_t st) {
@@ -1538,6 +1557,187 @@ hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st) {
 hipError_t launch_project(const AbsorbArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(k_project, dim3(kVdim / 64, kHeads, (a.n_q + kAbsorbRows - 1) / kAbsorbRows), dim3(256), 0,
                        st, a);
+    return hipGetLastError();
+}
+}  // namespace dsa
+
+// ---------------------------------------------------------------- indexer input preparation
+// Rope on the tail 64 dimensions, then the orthonormal Walsh-Hadamard
+// rotation, then rounding to the indexer's 16-bit format, for the indexer
+// queries of a step and for the keys it appends to the key cache.  A wave
+// takes four 128-wide vectors side by side.  Vector s (lane bits 2-3) is
+// spread over 16 lanes; its piece c (dimensions 8c .. 8c+7, two 16-byte
+// loads and one 16-byte store) sits on lane (c & 3) | 4 s | 16 (c >> 2).
+// Dimension bits 0-2 are inside the lane: three butterfly stages in
+// registers.  Bits 3-4 are lane bits 0-1, whose partner comes by DPP within
+// the quad; bits 5-6 are lane bits 4-5, whose pairs permlane16/32_swap hand
+// over as (lower lane's value, upper lane's value), so each stage element is
+// one multiply-add.  The rope slice is lanes 32-63; pair (64+2j, 65+2j)
+// lies inside the lane holding piece 8 + j/4.  The (cos, sin) of every pair
+// a wave needs is computed once into a per-wave LDS table: 32 entries when
+// the four vectors are heads of one query (one position), 4 x 32 otherwise.
+// Angles are formed and reduced modulo pi/2 in double (pair 0 turns by the
+// position in radians, up to 2^31), and the reduced angle, at most pi/4,
+// goes through Taylor polynomials in float (truncation below 2e-9).
+namespace dsa {
+constexpr int kPrepRows = 4;   // vectors per wave
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// (cos t, sin t) for t = pos * inv_freq radians
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, double inv_freq) {
+    const double t = (double)pos * inv_freq;
+    const double q = rint(t * 0.6366197723675814);                       // 2 / pi
+    double rd = fma(-q, 1.5707963267948966, t);                           // pi / 2, high part
+    rd = fma(-q, 6.123233995736766e-17, rd);                              // pi / 2, low part
+    const float r = (float)rd, r2 = r * r;
+    // sin r = r - r^3/3! + ... + r^9/9!,  cos r = 1 - r^2/2! + ... - r^10/10!
+    float sp = 2.7557319e-6f;                                             // 1/9!
+    sp = fmaf(sp, r2, -1.9841270e-4f);                                   // 1/7!
+    sp = fmaf(sp, r2, 8.3333333e-3f);                                    // 1/5!
+    sp = fmaf(sp, r2, -1.6666667e-1f);                                   // 1/3!
+    const float sr = fmaf(sp * r2, r, r);
+    float cp = -2.7557319e-7f;                                            // 1/10!
+    cp = fmaf(cp, r2, 2.4801587e-5f);                                    // 1/8!
+    cp = fmaf(cp, r2, -1.3888889e-3f);                                   // 1/6!
+    cp = fmaf(cp, r2, 4.1666667e-2f);                                    // 1/4!
+    cp = fmaf(cp, r2, -0.5f);
+    const float cr = fmaf(cp, r2, 1.f);
+    const int n = (int)((int64_t)q & 3);                                  // quadrant
+    const float c = (n & 1) ? sr : cr, s_ = (n & 1) ? cr : sr;
+    return make_float2((n == 1 || n == 2) ? -c : c, (n >= 2) ? -s_ : s_);
+}
+
+__global__ __launch_bounds__(256) void k_index_prep(PrepArgs a) {
+    __shared__ float2 tab[4][kPrepRows][32];       // per wave: (cos, sin) of (vector, pair)
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const int sv = (lane >> 2) & 3;                 // vector of the wave
+    const int c = (lane & 3) | ((lane >> 4) << 2);  // piece of the vector
+    const int64_t n_qv = (int64_t)a.n_q * kIdxHeads;
+    const int64_t total = n_qv + a.n_new;
+    const int64_t v0 = ((int64_t)blockIdx.x * 4 + w) * kPrepRows;
+    if (v0 >= total) return;
+    const int64_t v = v0 + sv;
+
+    const float *src = nullptr;
+    uint16_t *dst = nullptr;
+    int64_t pos = 0;
+    if (v < n_qv) {
+        pos = (int64_t)a.q_nvis[v / kIdxHeads] - 1;
+        src = a.q_in + v * kIdxDim;
+        dst = a.q_out + v * kIdxDim;
+    } else if (v < total) {
+        // the key's own row is read before its destination is known
+        const int64_t k = v - n_qv;
+        src = a.k_in + k * kIdxDim;
+        const int64_t seq = a.k_seq ? a.k_seq[k] : k;
+        const int64_t p = a.k_pos[k];
+        pos = p;
+        if (seq >= 0 && seq < a.n_seq && p >= 0 && p < a.key_stride)
+            dst = a.k_cache + (seq * a.key_stride + p) * kIdxDim;
+    }
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+    if (src) {
+        x0 = __builtin_nontemporal_load((const f32x4 *)(src + 8 * c));
+        x1 = __builtin_nontemporal_load((const f32x4 *)(src + 8 * c + 4));
+    }
+    float e[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+
+    if (a.rope) {
+        // the four vectors' positions (piece 0 of vector r is lane 4 r), and
+        // the frequency of pair j = lane & 31: the host's base^(-4i/32) for
+        // i = j/4, times base^(-1/32) per further step
+        int64_t pv[kPrepRows];
+#pragma unroll
+        for (int r = 0; r < kPrepRows; r++) {
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pos, 4 * r);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)pos >> 32), 4 * r);
+            pv[r] = (int64_t)(((uint64_t)hi << 32) | lo);
+        }
+        const int j = lane & 31;
+        double inv_freq = a.inv_freq[0];
+#pragma unroll
+        for (int i = 1; i < 8; i++) inv_freq = (j >> 2) == i ? a.inv_freq[i] : inv_freq;
+#pragma unroll
+        for (int m = 1; m < 4; m++) inv_freq = (j & 3) >= m ? inv_freq * a.freq_ratio : inv_freq;
+        const bool one_pos = v0 + kPrepRows <= n_qv;   // four heads of one query
+        if (one_pos) {
+            if (lane < 32) tab[w][0][j] = rope_cos_sin(pv[0], inv_freq);
+        } else {
+            const int r0 = lane >> 5;
+            tab[w][r0][j] = rope_cos_sin(r0 ? pv[1] : pv[0], inv_freq);
+            tab[w][r0 + 2][j] = rope_cos_sin(r0 ? pv[3] : pv[2], inv_freq);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        if (lane >= 32) {
+            const float2 *cs = &tab[w][one_pos ? 0 : sv][4 * (c - 8)];
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const float2 t = cs[m];
+                const float a0 = e[2 * m], b0 = e[2 * m + 1];
+                e[2 * m] = a0 * t.x - b0 * t.y;
+                e[2 * m + 1] = a0 * t.y + b0 * t.x;
+            }
+        }
+    }
+    // dimension bits 0-2: inside the lane
+#pragma unroll
+    for (int b = 1; b < 8; b <<= 1) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            if (k & b) continue;
+            const float lo = e[k], hi = e[k | b];
+            e[k] = lo + hi;
+            e[k | b] = lo - hi;
+        }
+    }
+    // bits 3-4: lane bits 0-1, partner by DPP (lower: own + partner, upper:
+    // partner - own)
+    const float s0 = (lane & 1) ? -1.f : 1.f, s1 = (lane & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) e[k] = s0 * e[k] + dpp_mov<0xB1>(e[k]);      // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int k = 0; k < 8; k++) e[k] = s1 * e[k] + dpp_mov<0x4E>(e[k]);      // quad_perm [2,3,0,1]
+    // bits 5-6: lane bits 4-5; the swap gives (lower lane's, upper lane's)
+    const float s4 = (lane & 16) ? -1.f : 1.f, s5 = (lane & 32) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(e[k]), __float_as_uint(e[k]), false, false);
+        e[k] = fmaf(s4, __uint_as_float(p[1]), __uint_as_float(p[0]));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(e[k]), __float_as_uint(e[k]), false, false);
+        e[k] = fmaf(s5, __uint_as_float(p[1]), __uint_as_float(p[0]));
+    }
+
+    if (!dst) return;
+    const float norm = 0.08838834764831845f;   // 1 / sqrt(128)
+    u32x4 packed;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const float y0 = e[2 * k] * norm, y1 = e[2 * k + 1] * norm;
+        if (a.f16)
+            packed[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
+        else
+            packed[k] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y1) << 16);
+    }
+    *(u32x4 *)(dst + 8 * c) = packed;
+}
+
+hipError_t launch_index_prep(const PrepArgs &a, hipStream_t st) {
+    const int64_t total = (int64_t)a.n_q * kIdxHeads + a.n_new;
+    const int64_t per_block = 4 * kPrepRows;
+    const unsigned blocks = (unsigned)((total + per_block - 1) / per_block);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_index_prep, dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 }  // namespace dsa

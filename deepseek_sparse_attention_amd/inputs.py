@@ -233,3 +233,18 @@ def c3_small(**kw) -> Workload:
     """Prefill variant whose chunk sits at positions 0..511 of a 4096-token
     context, so that early queries keep fewer than top-k candidates."""
     return make_workload("c3s", 13, GEOM_TOKEN, 1, 4096, np.zeros(512), np.arange(512) + 1, **kw)
+
+
+def indexer_projections(seed: int, n_q: int, n_new: int, n_idx_heads: int = 32, d_idx: int = 128,
+                        outliers: int = 4, outlier_scale: float = 16.0):
+    """Float32 indexer projections before their preparation: queries
+    [n_q, n_idx_heads, d_idx] and keys [n_new, d_idx], standard normal, with
+    ``outliers`` channels (the same ones for queries and keys) scaled by
+    ``outlier_scale``: the few large channels that make per-element rounding
+    uneven, which the rotation spreads out."""
+    rng = np.random.default_rng(seed)
+    scale = np.ones(d_idx, np.float32)
+    scale[rng.permutation(d_idx)[:outliers]] = outlier_scale
+    q = rng.standard_normal((n_q, n_idx_heads, d_idx), dtype=np.float32) * scale
+    k = rng.standard_normal((n_new, d_idx), dtype=np.float32) * scale
+    return q, k

@@ -79,8 +79,9 @@ enum {
  * d_latent 512, d_rope 64 (token-level rows of 576) or 0 (NoPE rows of 512),
  * n_idx_heads 32, d_idx 128, kpool 1 (rows are tokens) or 4 (rows are pools),
  * 1 <= top_k <= 4096 with top_k a multiple of kpool, softmax_scale finite
- * and > 0 (the pages' value is 1/16).  Anything else returns
- * DSA_ERR_UNSUPPORTED rather than being approximated. */
+ * and > 0 (the pages' value is 1/16), idx_f16 0 or 1 (1 only with kpool 1).
+ * Anything else returns DSA_ERR_UNSUPPORTED rather than being approximated.
+ * Zero-initialise the struct so that fields added later read as 0. */
 typedef struct {
     int32_t n_heads;        /* query heads (64)                                   */
     int32_t d_latent;       /* latent width = V width = output width (512)        */
@@ -90,6 +91,10 @@ typedef struct {
     int32_t top_k;          /* tokens kept per query (2048)                       */
     int32_t kpool;          /* tokens per indexer row: 1, or 4 for k-pool         */
     float softmax_scale;    /* multiplies the full (d_latent + d_rope) dot (1/16) */
+    int32_t idx_f16;        /* 16-bit format of the indexer queries and keys:
+                               0 bf16, 1 IEEE f16 (TensorSharp2 "The
+                               sparse-attention path": the indexer key cache
+                               is F16).  Every other 16-bit tensor is bf16.   */
 } dsa_geometry;
 
 /* The queries of one call.  A decode batch has one query per sequence with
@@ -121,12 +126,14 @@ int dsa_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 /* 1. Indexer scores.
  *   scores[q][r] = sum_h idx_w[q][h] * max(0, sum_d idx_q[q][h][d] * idx_k[seq(q)][r][d])
  * for r < rows(q); other entries of the row are not written.
- *   idx_q  [n_q][n_idx_heads][d_idx] bf16     idx_w [n_q][n_idx_heads] fp32
- *   idx_k  [n_seq][key_seq_stride][d_idx] bf16 (tokens, or pool keys for kpool 4;
- *          key_seq_stride >= max_nvis / kpool)
+ *   idx_q  [n_q][n_idx_heads][d_idx] 16-bit    idx_w [n_q][n_idx_heads] fp32
+ *   idx_k  [n_seq][key_seq_stride][d_idx] 16-bit (tokens, or pool keys for
+ *          kpool 4; key_seq_stride >= max_nvis / kpool)
  *   scores [n_q][score_ld] fp32, score_ld >= max_nvis / kpool.
- * Accumulation is fp32 over exact bf16 products; with integer-valued inputs
- * whose partial sums stay below 2^24 the result is exact. */
+ * idx_q and idx_k are bf16, or IEEE f16 when geom->idx_f16 (the same holds
+ * for dsa_decode_step).  Accumulation is fp32 over exact products; with
+ * integer-valued inputs whose partial sums stay below 2^24 the result is
+ * exact. */
 int dsa_index_scores(const dsa_geometry *geom, const dsa_batch *batch,
                      const dsa_bf16 *idx_q, const float *idx_w,
                      const dsa_bf16 *idx_k, int64_t key_seq_stride,
@@ -222,6 +229,37 @@ int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const 
  * enters the bf16 MFMA as two halves (truncated value + rounded
  * remainder); |error| <= 2^-14 * sum_j |o_j w_ij|. */
 int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float *ctx, hipStream_t stream);
+
+/* 7. Indexer input preparation (TensorSharp2 "The sparse-attention path":
+ * past top_k the indexer turns its queries and keys by rope and then by a
+ * Walsh-Hadamard rotation before scoring, and caches its keys as F16;
+ * table "The block": RoPE NORM, base 8e6, no YaRN, 64 rope dimensions).
+ * Every 128-wide vector x at position p becomes, in fp32,
+ *   rope (geom->d_rope = 64): for j < 32 the pair (x[64+2j], x[65+2j]) turns
+ *     by t = p * rope_base^(-j/32):  (a, b) -> (a cos t - b sin t, a sin t + b cos t)
+ *   rotation: y[i] = 128^(-1/2) * sum_k (-1)^popcount(i & k) * x[k]
+ * and is rounded to nearest even in the indexer format (geom->idx_f16).
+ * The angle is reduced modulo pi/2 in double before its sine and cosine.
+ *   queries  query q (batch->n_q of them) sits at position q_nvis[q] - 1:
+ *            q_in [n_q][32][128] fp32 -> q_out [n_q][32][128] 16-bit.  Both
+ *            NULL: no queries are prepared.
+ *   keys     key i < n_new sits at position k_pos[i] of sequence k_seq[i]
+ *            (i when k_seq is NULL; then n_new <= batch->n_seq) and is
+ *            written to row idx_k[seq][pos]: k_in [n_new][128] fp32 ->
+ *            idx_k [batch->n_seq][key_seq_stride][128] 16-bit.  A key whose
+ *            sequence is outside [0, n_seq) or position outside
+ *            [0, key_seq_stride) is not written; no other row is touched.
+ * Only kpool 1 is supported (DSA_ERR_UNSUPPORTED otherwise): the pages do
+ * not say that the pooled variant's keys are rotated.  rope_base must be
+ * finite and > 1.  Inputs and outputs must not overlap.  batch->max_nvis and
+ * q_per_seq_hint are not used.  No workspace.  Errors as for the calls
+ * above.  Each output is within half a unit in the last place of the 16-bit
+ * format, plus 2^-20 * sum_k |x_k| / sqrt(128), of the exact transform.  Two
+ * keys aimed at one row leave either of them there. */
+int dsa_index_prepare(const dsa_geometry *geom, const dsa_batch *batch, double rope_base,
+                      const float *q_in, dsa_bf16 *q_out,
+                      int32_t n_new, const int32_t *k_seq, const int32_t *k_pos, const float *k_in,
+                      dsa_bf16 *idx_k, int64_t key_seq_stride, hipStream_t stream);
 
 /* Instrumentation for benchmarks.  With events set (n_events > 0), each
  * dsa_decode_step call on this thread records events[0] on its stream before
