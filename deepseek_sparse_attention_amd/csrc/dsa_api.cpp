@@ -131,6 +131,7 @@ dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &
     a.cand_cap = p.cand_cap;
     a.split_rows = p.split_rows;
     a.n_split = p.n_split;
+    a.attn_hs = p.attn_hs;
     a.score_tile = p.score_tile;
     a.prefill = b->q_per_seq_hint >= 2 ? 1 : 0;
     a.pf_run = b->q_per_seq_hint;

@@ -41,6 +41,7 @@ struct Args {
     int32_t prefill;      // 1: queries come in runs of pf_run that share a sequence
     int32_t pf_run;       // queries per run (>= 2 when prefill)
     int32_t idx_f16;      // indexer queries and keys are IEEE f16 (else bf16)
+    int32_t attn_hs;      // attention by k_attend_hs (head groups of 16) instead of k_attend
 };
 
 // Arguments of the k-pool key producer.

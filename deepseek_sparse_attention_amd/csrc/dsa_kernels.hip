@@ -1231,6 +1231,235 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
     }
 }
 
+// Head-split attention for small batches.  One work-group = (head group hg
+// of 16 heads, query q, split sp), 512 threads: a few queries still fill the
+// chip, and the split partials shrink by the head factor.  The four head
+// groups of a (query, split) sit on the same XCD (work-groups are dealt to
+// XCDs round-robin; the head group is the slowest index over a pair count
+// padded to a multiple of 8), so their shared rows come from L2.  Rows
+// arrive by the same DMA ring as in k_attend.  Per step and wave w:
+//   QK : row block rt = w & 1 (16 rows), dimension part kq = w >> 1 (a
+//        quarter of the k-steps), S^T partial on MFMA 16x16x32 with the
+//        queries of that part in registers; the four parts of each row block
+//        are summed through LDS, so every wave holds S^T for all 32 rows;
+//   softmax: as in k_attend (every wave, per head = lane column);
+//   PV : O^T[col][head] += V^T P^T for the wave's 64 columns (4 blocks).
+template <int D>
+__global__ __launch_bounds__(512) void k_attend_hs(Args a) {
+    using Cfg = AttnCfg<D>;
+    constexpr int NKQ = (Cfg::ND + 3) / 4;        // most k-steps of a part
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::NBUF * Cfg::BUF];
+    __shared__ int32_t sidx[kMaxSplitRows];
+    __shared__ f32x4 sx[8][64];                    // partial scores per wave
+    const int pairs = a.n_q * a.n_split;
+    const int pairs8 = (pairs + 7) & ~7;
+    const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
+    if (pair >= pairs) return;
+    const int q = pair / a.n_split, sp = pair % a.n_split;
+    const QInfo qi = query_info(a, q);
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rt = w & 1, kq = w >> 1;
+    const int kcnt = Cfg::ND / 4 + (kq < Cfg::ND % 4 ? 1 : 0);
+    const int k0 = kq * (Cfg::ND / 4) + (kq < Cfg::ND % 4 ? kq : Cfg::ND % 4);
+    const int head = 16 * hg + n;
+
+    // a count outside [0, top_k + kpool - 1] makes the query invalid
+    int32_t count = 0;
+    bool invalid = qi.mode == 2;
+    if (!invalid) {
+        count = a.sel_count[q];
+        if (count < 0 || count > a.top_k + a.kpool - 1) {
+            invalid = true;
+            count = 0;
+        }
+    }
+    const int32_t start = sp * a.split_rows;
+    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
+    const int nst = (nrows + kAttnRows - 1) / kAttnRows;
+    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
+
+    {
+        const int32_t *selq = a.sel + (size_t)q * a.sel_ld + start;
+        for (int r = threadIdx.x; r < nst * kAttnRows; r += 512) {
+            int32_t t = -1;
+            if (r < nrows) {
+                t = selq[r];
+                if (t < 0 || (int64_t)t >= a.cache_stride) t = -1;
+            }
+            sidx[r] = t;
+        }
+    }
+    // this wave's queries: k-steps k0 .. k0 + kcnt - 1 of heads 16 hg ..
+    bf16x8 qreg[NKQ];
+    {
+        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 32 * k0 + 8 * g;
+#pragma unroll
+        for (int j = 0; j < NKQ; j++)
+            qreg[j] = j < kcnt ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j)) : bf16x8{};
+#pragma unroll
+        for (int j = 0; j < NKQ; j++) asm volatile("" ::"v"(qreg[j]));
+    }
+    __syncthreads();
+
+    const bool rope_wave = D > 512 && w < 4;
+    auto issue = [&](int32_t iv, int32_t ir, int b) {
+        uint8_t *vb = lds + b * Cfg::BUF;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = w + 8 * i;
+            const int32_t t = __builtin_amdgcn_readlane(iv, r);
+            const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
+            dma16(src + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(vb + r * Cfg::VS)));
+        }
+        if (rope_wave) {
+            const int row = 8 * w + (lane >> 3);
+            const uint8_t *src = ir >= 0 ? C + (size_t)ir * (2 * D) : kZeroRow;
+            const int piece = (lane & 7) ^ (row & 7);
+            dma16(src + 1024 + 16 * piece, __builtin_amdgcn_readfirstlane(lds_addr(vb + Cfg::VBYTES + 8 * w * 128)));
+        }
+    };
+    auto idx_v = [&](int c) -> int32_t { return c < nst ? sidx[kAttnRows * c + (lane & 31)] : -1; };
+    auto idx_r = [&](int c) -> int32_t { return c < nst ? sidx[kAttnRows * c + 8 * (w & 3) + (lane >> 3)] : -1; };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_part = 0.f;
+
+    int32_t iv_cur = idx_v(0), iv_n1 = idx_v(1), iv_n2 = idx_v(2), ir_n2 = idx_r(2);
+    if (nst > 0) issue(iv_cur, idx_r(0), 0);
+    if (nst > 1) issue(iv_n1, idx_r(1), 1);
+    int b_cur = 0;
+    for (int c = 0; c < nst; c++) {
+        if (c + 1 < nst) {
+            if (rope_wave)
+                wait_vm<5>();
+            else
+                wait_vm<4>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();
+        if (c + 2 < nst) issue(iv_n2, ir_n2, b_cur == 0 ? 2 : b_cur - 1);
+        const uint8_t *vb = lds + b_cur * Cfg::BUF;
+        b_cur = b_cur == 2 ? 0 : b_cur + 1;
+        const uint64_t okmask = __ballot(lane < kAttnRows && iv_cur >= 0);
+        iv_cur = iv_n1;
+        iv_n1 = iv_n2;
+        iv_n2 = idx_v(c + 3);
+        ir_n2 = idx_r(c + 3);
+
+        // partial S^T of row block rt over this wave's k-steps
+        f32x4 sp_acc = {0.f, 0.f, 0.f, 0.f};
+        {
+            bf16x8 ra[NKQ];
+#pragma unroll
+            for (int j = 0; j < NKQ; j++) {
+                const int s = k0 + j;
+                const uint8_t *p0;
+                if (D > 512 && s >= 16) {
+                    const int pc = 4 * (s - 16) + g;
+                    p0 = vb + Cfg::VBYTES + (16 * rt + n) * 128 + 16 * (pc ^ (n & 7));
+                } else {
+                    p0 = vb + (16 * rt + n) * Cfg::VS + 64 * s + 16 * g;
+                }
+                ra[j] = j < kcnt ? __builtin_bit_cast(bf16x8, *(const u32x4 *)p0) : bf16x8{};
+            }
+#pragma unroll
+            for (int j = 0; j < NKQ; j++)
+                if (j < kcnt) sp_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[j], qreg[j], sp_acc, 0, 0, 0);
+        }
+        sx[w][lane] = sp_acc;
+        lds_barrier();
+        f32x4 s0 = sx[0][lane], s1 = sx[1][lane];
+#pragma unroll
+        for (int k = 1; k < 4; k++) {
+            s0 += sx[2 * k][lane];
+            s1 += sx[2 * k + 1][lane];
+        }
+
+        // online softmax over this step's rows, per head (lane column n);
+        // element j of this lane is row 4g + j (j < 4) or 16 + 4g + j - 4
+        float z[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int rr = (j < 4 ? 0 : 16) + 4 * g + (j & 3);
+            const float sv = j < 4 ? s0[j] : s1[j - 4];
+            const float v = ((okmask >> rr) & 1) ? sv * a.scale_log2 : -INFINITY;
+            z[j] = v;
+            cmax = fmaxf(cmax, v);
+        }
+        cmax = xor16_max(cmax);
+        cmax = xor32_max(cmax);
+        const bool need = cmax > m_ref + 8.f;
+        if (__any(need)) {
+            const float m_new = need ? cmax : m_ref;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+            m_ref = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[i] *= alpha;
+        }
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float p = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[j] - m_ref);
+            l_part += p;
+            const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
+            const float lo = p - __uint_as_float(hb);
+            phi[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+            plo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(lo) >> 16));
+        }
+        // O^T += V^T P^T over this wave's 4 column blocks of 16
+        {
+            const int r_in = n >> 2, c_in = n & 3;
+            const uint8_t *v1 = vb + (4 * g + r_in) * Cfg::VS + 8 * c_in + 128 * w;
+            const uint8_t *v2 = vb + (16 + 4 * g + r_in) * Cfg::VS + 8 * c_in + 128 * w;
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            bf16x8 av[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; cb++) {
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v1 + 32 * cb));
+                const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v2 + 32 * cb));
+                const i16x8 tv = {t1[0], t1[1], t1[2], t1[3], t2[0], t2[1], t2[2], t2[3]};
+                av[cb] = __builtin_bit_cast(bf16x8, tv);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 4; cb++) {
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cb], phi, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cb], plo, acc[cb], 0, 0, 0);
+            }
+        }
+    }
+    const float l_tot = xor32_sum(xor16_sum(l_part));
+
+    const int col0 = 64 * w + 4 * g;
+    if (a.n_split == 1) {
+        const bool bad = invalid || l_tot == 0.f;
+        const float inv = 1.f / l_tot;
+        float *o = a.out + ((size_t)q * kHeads + head) * kLatent + col0;
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) {
+            f32x4 val = acc[cb] * inv;
+            if (bad) val = f32x4{NAN, NAN, NAN, NAN};
+            *(f32x4 *)(o + 16 * cb) = val;
+        }
+        if (a.lse && w == 0 && g == 0)
+            a.lse[(size_t)q * kHeads + head] = bad ? NAN : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+    } else {
+        const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + head;
+        float *o = a.pacc + slot * kLatent + col0;
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) *(f32x4 *)(o + 16 * cb) = acc[cb];
+        if (w == 0 && g == 0) {
+            a.pml[2 * slot] = m_ref;
+            a.pml[2 * slot + 1] = l_tot;
+        }
+    }
+}
+
 // Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
 // thread four output columns.  Up to 16 splits are loaded in one round trip
 // and merged online (running max, rescaled sums).
@@ -1526,10 +1755,17 @@ hipError_t launch_select(const Args &a, hipStream_t st) {
 }
 
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between) {
-    if (a.D == 576)
+    if (a.attn_hs) {
+        const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
+        if (a.D == 576)
+            hipLaunchKernelGGL(k_attend_hs<576>, dim3(4 * pairs8), dim3(512), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_attend_hs<512>, dim3(4 * pairs8), dim3(512), 0, st, a);
+    } else if (a.D == 576) {
         hipLaunchKernelGGL(k_attend<576>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
-    else
+    } else {
         hipLaunchKernelGGL(k_attend<512>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (between) between();
     if (e != hipSuccess || a.n_split == 1) return e;

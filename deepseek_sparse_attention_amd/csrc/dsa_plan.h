@@ -32,6 +32,7 @@ struct Plan {
     int32_t sel_max;              // top_k + kpool - 1
     int32_t split_rows;           // selected rows per attention work-group
     int32_t n_split;              // attention splits per query
+    int32_t attn_hs;              // 1: head-split attention kernel
     int32_t score_tile;           // key rows per score work-group
 
     // workspace byte offsets; [0, ctrl_bytes) must be zero between calls
@@ -65,10 +66,16 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
     p.cand_cap = p.chunk / 4;     // a chunk's candidates beyond this are found again by k_select
 
-    // attention splits: aim at ~128 (query, split) work-groups (one CU
-    // each), whole 32-row steps, 64..kMaxSplitRows rows per split; the
-    // environment variable DSA_ATTN_PAIRS overrides the target (tuning)
-    int64_t ns = (128 + n_q - 1) / n_q;
+    // attention: up to 64 queries run head-split (k_attend_hs: a work-group
+    // per head group of 16, query and split), aiming at ~64 (query, split)
+    // pairs = 256 work-groups; more queries run k_attend (all 64 heads per
+    // work-group), aiming at ~128 work-groups.  Whole 32-row steps,
+    // 64..kMaxSplitRows rows per split.  Tuning overrides from the
+    // environment: DSA_ATTN_HS (0 or 1) picks the kernel, DSA_ATTN_PAIRS the
+    // (query, split) target.
+    p.attn_hs = n_q <= 64 ? 1 : 0;
+    if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) ? 1 : 0;
+    int64_t ns = ((p.attn_hs ? 64 : 128) + n_q - 1) / n_q;
     if (const char *e = getenv("DSA_ATTN_PAIRS")) ns = (atoi(e) + n_q - 1) / n_q;
     int64_t sr = (p.sel_max + ns - 1) / ns;
     sr = (sr + 31) / 32 * 32;

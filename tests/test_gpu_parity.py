@@ -140,8 +140,12 @@ def test_topk_bit_exact(kind, kpool, top_k):
 
 @pytest.mark.parametrize("d_rope", [64, 0])
 @pytest.mark.parametrize("count", [1, 31, 32, 33, 100, 2048, 2051])
-def test_attend_matches_oracle(d_rope, count):
-    log(f"attend d_rope={d_rope} count={count}")
+@pytest.mark.parametrize("kernel", ["hs", "wide"])
+def test_attend_matches_oracle(d_rope, count, kernel, monkeypatch):
+    """Both attention kernels (head-split, and all heads per work-group),
+    forced by the planner's override, against the oracle."""
+    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    log(f"attend d_rope={d_rope} count={count} kernel={kernel}")
     rng = np.random.default_rng(count * 7 + d_rope)
     g = geom(kpool=4 if d_rope == 0 else 1, d_rope=d_rope)
     D = 512 + d_rope
@@ -189,10 +193,12 @@ def _attend_case(d_rope, n_q, sel, cnt, T, seed):
 
 
 @pytest.mark.parametrize("d_rope", [64, 0])
-def test_attend_skips_invalid_rows_and_counts(d_rope):
+@pytest.mark.parametrize("kernel", ["hs", "wide"])
+def test_attend_skips_invalid_rows_and_counts(d_rope, kernel, monkeypatch):
     """Entries outside [0, T) inside the count are skipped; a count outside
     [0, top_k + kpool - 1], or one that leaves no row, gives NaN."""
-    log(f"attend edge rows d_rope={d_rope}")
+    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    log(f"attend edge rows d_rope={d_rope} kernel={kernel}")
     rng = np.random.default_rng(91 + d_rope)
     T, n_q = 3000, 8
     kp = 4 if d_rope == 0 else 1
@@ -222,10 +228,12 @@ def test_attend_skips_invalid_rows_and_counts(d_rope):
         assert np.isnan(out[j]).all() and np.isnan(lse[j]).all(), f"query {j} should be NaN"
 
 
-def test_attend_single_split_path():
-    """Many queries: every query is one work-group that writes its output
-    directly (no split merge)."""
-    log("attend single split")
+@pytest.mark.parametrize("kernel", ["hs", "wide"])
+def test_attend_single_split_path(kernel, monkeypatch):
+    """Many queries: every query is one work-group (or four head groups)
+    that writes its output directly (no split merge)."""
+    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    log(f"attend single split kernel={kernel}")
     rng = np.random.default_rng(17)
     T, n_q = 2500, 300
     sel_ld = 2048
