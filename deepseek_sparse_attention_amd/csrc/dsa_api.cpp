@@ -132,6 +132,7 @@ dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &
     a.split_rows = p.split_rows;
     a.n_split = p.n_split;
     a.attn_hs = p.attn_hs;
+    a.select_scan = p.select_scan;
     a.score_tile = p.score_tile;
     a.prefill = b->q_per_seq_hint >= 2 ? 1 : 0;
     a.pf_run = b->q_per_seq_hint;
@@ -263,7 +264,7 @@ int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int
         a.sel_ld = sel_ld;
         a.sel_count = sel_count;
         DSA_TRY(launched(dsa::launch_hist(a, stream), "hist"));
-        DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
+        if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
         return launched(dsa::launch_select(a, stream), "select");
     });
 }
@@ -346,7 +347,7 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
         Timer tm(stream);
         DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream), "score"));
         tm.tick();
-        DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
+        if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
         tm.tick();
         DSA_TRY(launched(dsa::launch_select(a, stream), "select"));
         tm.tick();

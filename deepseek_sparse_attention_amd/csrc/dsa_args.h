@@ -42,6 +42,7 @@ struct Args {
     int32_t pf_run;       // queries per run (>= 2 when prefill)
     int32_t idx_f16;      // indexer queries and keys are IEEE f16 (else bf16)
     int32_t attn_hs;      // attention by k_attend_hs (head groups of 16) instead of k_attend
+    int32_t select_scan;  // k_select gathers its candidates itself (no k_filter)
 };
 
 // Arguments of the k-pool key producer.

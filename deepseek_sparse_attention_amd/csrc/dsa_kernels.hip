@@ -638,7 +638,7 @@ struct SelectShared {
     uint32_t h2[1024];
     uint32_t h3[1024];
     uint32_t tot[2][kSelWaves];
-    uint32_t res[2];
+    uint32_t res[3];
 };
 
 // Exclusive prefix sum over the 1024 threads with one barrier; the 16-word
@@ -664,7 +664,7 @@ __device__ __forceinline__ uint32_t sel_scan(uint32_t v, uint32_t *slot, uint32_
 // suffix(b) >= need > suffix(b + 1); above = suffix(b + 1).
 template <int PER>
 __device__ uint32_t sel_find(const uint32_t (&c)[PER], uint32_t need, uint32_t *slot, uint32_t *res,
-                             uint32_t &above) {
+                             uint32_t &above, uint32_t *in_bin = nullptr) {
     const int hi = kSelThreads * PER - PER * (int)threadIdx.x;
     uint32_t s = 0;
 #pragma unroll
@@ -672,7 +672,7 @@ __device__ uint32_t sel_find(const uint32_t (&c)[PER], uint32_t need, uint32_t *
     uint32_t total;
     const uint32_t before = sel_scan(s, slot, total);
     if (before < need && before + s >= need) {
-        uint32_t run = before, bin = 0, run_at = 0;
+        uint32_t run = before, bin = 0, run_at = 0, cnt = 0;
         bool found = false;
 #pragma unroll
         for (int i = 0; i < PER; i++) {
@@ -680,28 +680,45 @@ __device__ uint32_t sel_find(const uint32_t (&c)[PER], uint32_t need, uint32_t *
                 found = true;
                 bin = (uint32_t)(hi - 1 - i);
                 run_at = run;
+                cnt = c[i];
             }
             run += c[i];
         }
         res[0] = bin;
         res[1] = run_at;
+        res[2] = cnt;
     }
     __syncthreads();
     above = res[1];
     const uint32_t b = res[0];
+    if (in_bin) *in_bin = res[2];
     __syncthreads();
     return b;
 }
 
-// grid (n_q), 1024 threads.
+// grid (n_q), 1024 threads.  SCAN: the work-group finds the threshold
+// bucket from the first-digit histogram itself and gathers the candidates
+// by scanning the query's scores (no k_filter); otherwise k_filter's chunk
+// slots are gathered.
+template <bool SCAN>
 __global__ __launch_bounds__(kSelThreads) void k_select(Args a) {
     __shared__ SelectShared sh;
     const int q = blockIdx.x, tid = threadIdx.x;
     const QInfo qi = query_info(a, q);
     int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    // SCAN: thread t holds the first-digit counts of bins 4095 - 4t - i,
+    // read before it clears them
+    uint32_t c1[kHistBins / kSelThreads];
     {
         uint32_t *gh = a.hist + (size_t)q * kHistBins;
-        for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+        if (SCAN) {
+#pragma unroll
+            for (int i = 0; i < kHistBins / kSelThreads; i++) c1[i] = gh[kHistBins - 1 - 4 * tid - i];
+#pragma unroll
+            for (int i = 0; i < kHistBins / kSelThreads; i++) gh[kHistBins - 1 - 4 * tid - i] = 0;
+        } else {
+            for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+        }
     }
     if (qi.mode != 1) {
         const int32_t cnt = qi.mode == 0 ? qi.nvis : 0;
@@ -714,23 +731,81 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Args a) {
     const int64_t rows = qi.rows;
     const float *s = a.scores_in + (size_t)q * a.score_ld;
     const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
-    const uint32_t b1 = a.thr[2 * q], above1 = a.thr[2 * q + 1];
-    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
     int par = 0;                                    // alternates the scan slots
 
     for (int i = tid; i < 1024; i += kSelThreads) {
         sh.h2[i] = 0;
         sh.h3[i] = 0;
     }
+    uint32_t b1, above1, n_cand;
+    bool in_lds;
+    if (SCAN) {
+        // the first tile of scores in flight while the bucket is found
+        float v[kSelPer];
+        load_scores<kSelPer>(s, kSelPer * tid, rows, vec, v);
+        uint32_t in_b1;
+        b1 = sel_find<kHistBins / kSelThreads>(c1, keep, sh.tot[par++ & 1], sh.res, above1, &in_b1);
+        n_cand = above1 + in_b1;
+        in_lds = n_cand <= (uint32_t)kSelCap;
+        if (in_lds) {
+            // every row whose first digit is at least b1, in row order, with
+            // the second-digit histogram of bucket b1 on the way
+            uint32_t base = 0;
+            for (int64_t sb = 0; sb < rows; sb += kSelTile) {
+                const int64_t rb = sb + kSelPer * tid;
+                float vn[kSelPer];
+                if (sb + kSelTile < rows) load_scores<kSelPer>(s, rb + kSelTile, rows, vec, vn);
+                uint32_t keys[kSelPer];
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) {
+                    keys[i] = order_key(v[i]);
+                    const uint32_t d1 = keys[i] >> 20;
+                    if (rb + i < rows && d1 >= b1) {
+                        m |= 1u << i;
+                        if (d1 == b1) atomicAdd(&sh.h2[(keys[i] >> 10) & 1023], 1u);
+                    }
+                }
+                uint32_t tot;
+                uint32_t pos = base + sel_scan(__builtin_popcount(m), sh.tot[par++ & 1], tot);
+                base += tot;
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) {
+                    if (!((m >> i) & 1)) continue;
+                    if (pos < (uint32_t)kSelCap) {
+                        sh.key[pos] = keys[i];
+                        sh.row[pos] = (int32_t)(rb + i);
+                    }
+                    pos++;
+                }
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) v[i] = vn[i];
+            }
+        } else {
+            for (int64_t sb = 0; sb < rows; sb += kSelTile) {
+                const int64_t rb = sb + kSelPer * tid;
+                float w[kSelPer];
+                load_scores<kSelPer>(s, rb, rows, vec, w);
+#pragma unroll
+                for (int i = 0; i < kSelPer; i++) {
+                    const uint32_t k = order_key(w[i]);
+                    if (rb + i < rows && (k >> 20) == b1) atomicAdd(&sh.h2[(k >> 10) & 1023], 1u);
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+    b1 = a.thr[2 * q];
+    above1 = a.thr[2 * q + 1];
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
     // candidate counts per chunk -> row-ordered offsets
     const uint32_t *cc = a.chunk_cnt + (size_t)q * a.n_chunks;
     const uint32_t my_cnt = tid < nch ? cc[tid] : 0u;
-    uint32_t n_cand;
     const uint32_t my_pre = sel_scan(my_cnt, sh.tot[par++ & 1], n_cand);
     const bool any_ovf = __syncthreads_or(my_cnt > (uint32_t)a.cand_cap) != 0;
     if (tid < nch) sh.pre[tid] = my_pre;
     if (tid == 0) sh.pre[nch] = n_cand;
-    const bool in_lds = n_cand <= (uint32_t)kSelCap;
+    in_lds = n_cand <= (uint32_t)kSelCap;
     __syncthreads();
 
     if (in_lds) {
@@ -827,6 +902,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Args a) {
         }
     }
     __syncthreads();
+    }
 
     // second digit
     const uint32_t need2 = keep - above1;
@@ -1750,7 +1826,10 @@ hipError_t launch_filter(const Args &a, hipStream_t st) {
 }
 
 hipError_t launch_select(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_select, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
+    if (a.select_scan)
+        hipLaunchKernelGGL(k_select<true>, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_select<false>, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct Plan {
     int32_t split_rows;           // selected rows per attention work-group
     int32_t n_split;              // attention splits per query
     int32_t attn_hs;              // 1: head-split attention kernel
+    int32_t select_scan;          // 1: top-k in one kernel that scans the scores
     int32_t score_tile;           // key rows per score work-group
 
     // workspace byte offsets; [0, ctrl_bytes) must be zero between calls
@@ -83,6 +84,14 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     if (sr > kMaxSplitRows) sr = kMaxSplitRows;
     p.split_rows = (int32_t)sr;
     p.n_split = (int32_t)((p.sel_max + sr - 1) / sr);
+
+    // top-k: when a query's rows fit one 16,384-row tile, one work-group per
+    // query scans its scores (no k_filter); beyond that the scan is bound by
+    // one CU's load rate and the chunked k_filter + k_select pair is faster
+    // (8 x 64K rows: 64.1 vs 71.1 us per step).  DSA_SELECT_SCAN=0/1 forces
+    // either path.
+    p.select_scan = p.max_rows <= 16384 ? 1 : 0;
+    if (const char *e = getenv("DSA_SELECT_SCAN")) p.select_scan = atoi(e) ? 1 : 0;
 
     // score tiles: 1024 rows per work-group (4 waves x 4 iterations x 64 rows)
     p.score_tile = 1024;

@@ -109,10 +109,14 @@ def _scores_case(rng, kind, n):
 
 @pytest.mark.parametrize("kind", ["real", "ties", "zeros", "signed_zero", "negative"])
 @pytest.mark.parametrize("kpool,top_k", [(1, 2048), (1, 7), (4, 2048), (4, 16)])
-def test_topk_bit_exact(kind, kpool, top_k):
+@pytest.mark.parametrize("select", ["scan", "chunked"])
+def test_topk_bit_exact(kind, kpool, top_k, select, monkeypatch):
     """Standalone top-k on given scores, including a tie storm larger than the
-    candidate buffer (all-zero scores over 20000 rows) and -0.0 / +0.0."""
-    log(f"topk {kind} kpool={kpool} k={top_k}")
+    candidate buffer (all-zero scores over 20000 rows) and -0.0 / +0.0, by
+    both select paths (one kernel scanning the scores, or k_filter's chunk
+    slots gathered by k_select)."""
+    monkeypatch.setenv("DSA_SELECT_SCAN", "1" if select == "scan" else "0")
+    log(f"topk {kind} kpool={kpool} k={top_k} select={select}")
     rng = np.random.default_rng(abs(hash((kind, kpool, top_k))) % 2**32)
     g = geom(kpool=kpool, d_rope=0 if kpool == 4 else 64, top_k=top_k)
     nvis = np.array([80003, 20000, top_k + kpool - 1, top_k + kpool, 5], np.int32)
