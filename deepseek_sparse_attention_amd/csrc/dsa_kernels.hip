@@ -203,6 +203,14 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
 }
 
 // ---------------------------------------------------------------- scores
+// max(x, 0) in one integer max: a float with its sign bit set is a negative
+// int32, so every negative x (and -0) becomes +0 and every positive x stays.
+// fmaxf on an MFMA result costs a canonicalising max first.  Finite x only.
+__device__ __forceinline__ float relu(float x) {
+    const int32_t i = __float_as_int(x);
+    return __int_as_float(i > 0 ? i : 0);
+}
+
 // One 16x16x32 MFMA step of the indexer on 16-bit operands: bf16, or IEEE
 // f16 when F16 (the two formats of the indexer queries and key cache).
 template <bool F16>
@@ -221,8 +229,10 @@ __device__ __forceinline__ f32x4 mfma_idx(bf16x8 a, bf16x8 b, f32x4 c) {
 // (one wave instruction = 1 KiB = 4 rows), the next step's 16 KiB already in
 // flight in registers while the current one is computed; each step is staged
 // in the wave's own LDS tile with the 16-byte pieces of row r stored at
-// slot (piece ^ (r & 7)), so that both the row-major store and the MFMA
-// operand reads below are free of bank conflicts.  Per 16 rows:
+// slot (piece ^ (r & 15)), so that both the row-major store and the MFMA
+// operand reads below are free of bank conflicts (the LDS has 64 banks:
+// the 16 rows an MFMA operand read takes per 16-lane phase must land their
+// pieces in 16 different 16-byte slots).  Per 16 rows:
 // A = idx_q (heads x d, two 16-head blocks, from registers), B = keys^T
 // (d x rows): lane (g = l/16, n = l%16) takes row n, d in [32 s + 8 g, +8)
 // for k-step s.  D[head][row] lands as lane (g, n) holding heads 4g + r
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int r = 4 * i + (lane >> 4), pc = lane & 15;
-            *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 7))) = v[i];
+            *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 15))) = v[i];
         }
         if (base + 256 < end) fetch(base + 256);
         __builtin_amdgcn_wave_barrier();
@@ -294,15 +304,15 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
+                const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 15))));
                 acc0 = mfma_idx<F16>(qa[0][s], b, acc0);
                 acc1 = mfma_idx<F16>(qa[1][s], b, acc1);
             }
             float x = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 4; rr++) {
-                x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
-                x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
+                x += wt[0][rr] * relu(acc0[rr]);
+                x += wt[1][rr] * relu(acc1[rr]);
             }
             p[st] = x;
         }
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
         for (int i = 0; i < 4; i++) {
             const int e = threadIdx.x + 512 * i;
             const int r = e >> 4, pc = e & 15;
-            *(u32x4 *)(&ktile[buf][r * 256 + 16 * (pc ^ (r & 7))]) = v[i];
+            *(u32x4 *)(&ktile[buf][r * 256 + 16 * (pc ^ (r & 15))]) = v[i];
         }
     };
     // partial score of 16-row block rb of the tile: lane (g, n) holds row n's
@@ -426,15 +436,15 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 7))));
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const u32x4 *)(tb + r * 256 + 16 * ((4 * s + g) ^ (r & 15))));
             acc0 = mfma_idx<F16>(qa[0][s], bv, acc0);
             acc1 = mfma_idx<F16>(qa[1][s], bv, acc1);
         }
         float x = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
-            x += wt[0][rr] * fmaxf(acc0[rr], 0.f);
-            x += wt[1][rr] * fmaxf(acc1[rr], 0.f);
+            x += wt[0][rr] * relu(acc0[rr]);
+            x += wt[1][rr] * relu(acc1[rr]);
         }
         return x;
     };
