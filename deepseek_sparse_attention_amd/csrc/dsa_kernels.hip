@@ -340,23 +340,25 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
 }
 
 // Chunked-prefill / verify-window indexer: a dense [queries x 32 heads] x
-// [128 x keys] contraction per work-group.  grid (key ranges, blocks), 512
-// threads = 8 waves.  A block holds up to 8 consecutive queries of one run
-// (pf_block); they are positions of one sequence (the leader's), and a
-// query of another sequence is left to the fix-up pass of k_score.  Key
-// tiles of 128 rows are loaded with coalesced 16-byte loads (512 threads x
-// 4 = 32 KiB), staged swizzled in LDS (double buffer) and shared by the
+// [128 x keys] contraction per work-group.  grid (key ranges, blocks), 1024
+// threads = 16 waves (4 per SIMD: the LDS of one work-group fills the CU, so
+// latency is hidden inside it).  A block holds up to 8 consecutive queries of
+// one run (pf_block); they are positions of one sequence (the leader's), and
+// a query of another sequence is left to the fix-up pass of k_score.  Key
+// tiles of 128 rows are loaded with coalesced 16-byte loads (1024 threads x
+// 2 = 32 KiB), staged swizzled in LDS (double buffer) and shared by the
 // block's queries.  With P = the block's query count rounded up to a power
-// of two, wave w computes query w * P / 8 on 16-row blocks [NB s, NB s + NB)
-// of each tile, NB = P and s = w % (8 / P): every wave has work however few
-// queries the block holds.  Causality masks the scores and the histogram
+// of two, wave w computes query w * P / 16 on 16-row blocks [NB s, NB s + NB)
+// of each tile, NB = max(1, P / 2) and s = w % (16 / P): every wave has work
+// however few queries the block holds, except half of them for a lone query.  Causality masks the scores and the histogram
 // per query (a query scores rows < rows(q)).  Per-query first-digit
 // histograms live in LDS as 16-bit counters, two to a word.
 constexpr int kPfTile = 128;     // key rows per LDS tile
 constexpr int kPfRange = 4096;   // key rows per work-group
+constexpr int kPfWaves = 16;     // waves per work-group (two per query of a full block)
 
 template <bool F16>
-__global__ __launch_bounds__(512) void k_score_prefill(Args a) {
+__global__ __launch_bounds__(kPfWaves * 64) void k_score_prefill(Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kPfTile * 256];
     __shared__ uint32_t lh[kPfQ][kHistBins / 2];
     __shared__ int32_t sh_rows[kPfQ];
@@ -366,8 +368,8 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     if (q0 >= q_end) return;                 // past the last query
     const int nq = q_end - q0;
     const int P = nq > 4 ? 8 : (nq > 2 ? 4 : nq);
-    const int slot = w * P / kPfQ;           // this wave's query within the block
-    const int sl = w % (kPfQ / P);           // and its share of each tile
+    const int slot = w * P / kPfWaves;       // this wave's query within the block
+    const int sl = w % (kPfWaves / P);       // and its share of each tile
     const int q = q0 + slot;
     const int lead = query_seq(a, q0);
     const bool hist = a.fused != 0;
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     const int64_t k1 = k0 + kPfRange < kmax ? k0 + kPfRange : kmax;
     const int32_t my_rows = sh_rows[slot];
     if (hist)
-        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) (&lh[0][0])[i] = 0;
+        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += kPfWaves * 64) (&lh[0][0])[i] = 0;
 
     bf16x8 qa[2][4];
     float wt[2][4];
@@ -411,11 +413,12 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     float *srow = a.scores + (size_t)qv * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
 
-    u32x4 v[4];
+    constexpr int kPieces = kPfTile * 16 / (kPfWaves * 64);   // 16-byte pieces per thread
+    u32x4 v[kPieces];
     auto fetch = [&](int64_t base) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int e = threadIdx.x + 512 * i;        // 16-byte piece of the tile
+        for (int i = 0; i < kPieces; i++) {
+            const int e = threadIdx.x + kPfWaves * 64 * i;   // 16-byte piece of the tile
             int64_t r = base + (e >> 4);
             r = r < kmax ? r : kmax - 1;
             v[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (e & 15)));
@@ -423,8 +426,8 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
     };
     auto stage = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int e = threadIdx.x + 512 * i;
+        for (int i = 0; i < kPieces; i++) {
+            const int e = threadIdx.x + kPfWaves * 64 * i;
             const int r = e >> 4, pc = e & 15;
             *(u32x4 *)(&ktile[buf][r * 256 + 16 * (pc ^ (r & 15))]) = v[i];
         }
@@ -485,10 +488,11 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
                 }
             } else {
                 // one or two blocks: full sum over the lane groups, written
-                // by lane group 0
+                // by lane group 0 (a lone query leaves half the waves idle)
 #pragma unroll
                 for (int j = 0; j < NB; j++) {
                     const int rb = NB * sl + j;
+                    if (rb >= kPfTile / 16) break;
                     const float score = xor32_sum(xor16_sum(block_part(tb, rb)));
                     if (g == 0) emit(base + 16 * rb + n, score);
                 }
@@ -496,17 +500,17 @@ __global__ __launch_bounds__(512) void k_score_prefill(Args a) {
             __syncthreads();                              // buffer free for the tile after next
         }
     };
+    // 16-row blocks per wave: the tile's 8 blocks shared by each query's
+    // kPfWaves / P waves
     if (P == 8)
-        tiles(std::integral_constant<int, 8>());
-    else if (P == 4)
         tiles(std::integral_constant<int, 4>());
-    else if (P == 2)
+    else if (P == 4)
         tiles(std::integral_constant<int, 2>());
     else
         tiles(std::integral_constant<int, 1>());
     if (hist) {
         __syncthreads();
-        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += 512) {
+        for (int i = threadIdx.x; i < kPfQ * kHistBins / 2; i += kPfWaves * 64) {
             const int qq = q0 + i / (kHistBins / 2);
             const uint32_t word = (&lh[0][0])[i];
             if (!word || qq >= q_end) continue;
@@ -1807,7 +1811,7 @@ hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st) {
         const unsigned ranges = (unsigned)((max_rows + kPfRange - 1) / kPfRange);
         const unsigned runs = (unsigned)((a.n_q + a.pf_run - 1) / a.pf_run);
         const unsigned per = (unsigned)((a.pf_run + kPfQ - 1) / kPfQ);
-        hipLaunchKernelGGL(k_score_prefill<F16>, dim3(ranges, runs * per), dim3(512), 0, st, a);
+        hipLaunchKernelGGL(k_score_prefill<F16>, dim3(ranges, runs * per), dim3(kPfWaves * 64), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
