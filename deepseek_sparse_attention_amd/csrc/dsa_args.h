@@ -41,7 +41,7 @@ struct Args {
     int32_t prefill;      // 1: queries come in runs of pf_run that share a sequence
     int32_t pf_run;       // queries per run (>= 2 when prefill)
     int32_t idx_f16;      // indexer queries and keys are IEEE f16 (else bf16)
-    int32_t attn_hs;      // attention by k_attend_hs (head groups of 16) instead of k_attend
+    int32_t attn_hs;      // attention kernel: 0 k_attend, 1 k_attend_hs, 2 k_attend_wv
     int32_t select_scan;  // k_select gathers its candidates itself (no k_filter)
 };
 

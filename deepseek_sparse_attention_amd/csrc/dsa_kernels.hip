@@ -1077,6 +1077,11 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
 }
 
+// The same with a uniform base address in SGPRs and a per-lane 32-bit offset.
+__device__ __forceinline__ void dma16s(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -1550,6 +1555,290 @@ __global__ __launch_bounds__(512) void k_attend_hs(Args a) {
     }
 }
 
+// Attention with wave-private rows, for small batches.  Same grid as
+// k_attend_hs (head group hg, query q, split sp; the four head groups of a
+// (query, split) on one XCD), but 256 threads whose 4 waves share nothing
+// inside the row loop: the split's rows go in 16-row steps to the waves in
+// turn (step s to wave s % 4).  Each wave DMAs its own steps into its own
+// two LDS buffers (the layout of k_attend, 16 rows), waits for them with
+// its own vmcnt and no barrier, and per step
+//   QK : S^T[16 rows][16 heads] over all D dimensions on MFMA 16x16x32
+//        (A = rows from LDS, B = the queries, all k-steps in registers);
+//   softmax: online per head, lazy rescale as in k_attend;
+//   PV : O^T[col][head] += V^T P^T for all 512 columns.  The hi and lo
+//        bf16 halves of P form the 32-deep K of one MFMA: lane group g
+//        holds P of rows 4g..4g+3 (the S^T accumulator layout) as
+//        (hi, hi, hi, hi, lo, lo, lo, lo), and A repeats the same four V
+//        rows, read by one ds_read_b64_tr_b16, in both halves.
+// The four waves' (max, sum, O) are merged through LDS once at the end.
+constexpr int kWvRows = 16;   // rows per step of one wave
+
+template <int D>
+struct WvCfg {
+    static constexpr int ND = D / 32;                       // MFMA k-steps of the score
+    static constexpr int VS = 1056;                         // LDS stride of a V row (bytes)
+    static constexpr int VBYTES = kWvRows * VS;
+    static constexpr int RBYTES = D > 512 ? kWvRows * 128 : 0;
+    static constexpr int BUF = VBYTES + RBYTES;
+    static constexpr int WAVE = 2 * BUF;                    // one wave's two buffers
+    static constexpr int NDMA = kWvRows + RBYTES / 1024;    // DMA instructions per step
+    static constexpr int OS = 516;                          // floats per head row of the merge
+};
+static_assert(4 * 16 * WvCfg<512>::OS * 4 <= 4 * WvCfg<512>::WAVE, "merge fits the row buffers");
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attend_wv(Args a) {
+    using Cfg = WvCfg<D>;
+    constexpr int kPer = kWvMaxRows / 256;                  // row indices per thread
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Cfg::WAVE];
+    __shared__ int32_t sidx[kWvMaxRows];
+    __shared__ float smx[4][16], ssum[4][16];
+    const int pairs = a.n_q * a.n_split;
+    const int pairs8 = (pairs + 7) & ~7;
+    const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
+    if (pair >= pairs) return;
+    const int q = pair / a.n_split, sp = pair % a.n_split;
+    const int32_t count_in = a.sel_count[q];   // issued with the query's own loads
+    const QInfo qi = query_info(a, q);
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int head = 16 * hg + n;
+    const int32_t start = sp * a.split_rows;
+
+    // The count, the split's row indices and the queries are loaded in one
+    // round trip; indices past the count are read (inside the caller's row
+    // stride) and dropped once the count is known.  Wave w reads the indices
+    // of its own steps w, w + 4, ...: lane l of rix[i] holds row l & 15 of
+    // the wave's step 4 i + l / 16, and the wave keeps them in its own part
+    // of sidx, so no barrier is needed before its first DMA.
+    int32_t rix[kPer];
+    {
+        const int32_t *selq = a.sel + (size_t)q * a.sel_ld + start;
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
+            rix[i] = (r < a.split_rows && start + r < a.sel_ld) ? selq[r] : -1;
+        }
+    }
+    bf16x8 qreg[Cfg::ND];
+    {
+        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 8 * g;
+#pragma unroll
+        for (int j = 0; j < Cfg::ND; j++) qreg[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j));
+    }
+    // a count outside [0, top_k + kpool - 1] makes the query invalid
+    const bool invalid = qi.mode == 2 || count_in < 0 || count_in > a.top_k + a.kpool - 1;
+    const int32_t count = invalid ? 0 : count_in;
+    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
+    const int nst = (nrows + kWvRows - 1) / kWvRows;
+    const int nj = nst > w ? (nst - w + 3) / 4 : 0;   // this wave's steps w, w + 4, ...
+    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
+        int32_t t = rix[i];
+        if (r >= nrows || t < 0 || (int64_t)t >= a.cache_stride) t = -1;
+        if (4 * i + g < nj) sidx[r] = t;
+    }
+
+    uint8_t *wb = lds + w * Cfg::WAVE;
+    const uint32_t voff = 16 * lane;
+    const uint32_t wb_lds = __builtin_amdgcn_readfirstlane(lds_addr(wb));
+    const uint64_t c_base = reinterpret_cast<uint64_t>(C), z_base = reinterpret_cast<uint64_t>(kZeroRow);
+    // address of row t, or of the zero row for t < 0, without a branch
+    auto row_addr = [&](int32_t t) -> uint64_t {
+        const uint64_t m = (uint64_t)(int64_t)(t >> 31);
+        return ((c_base + (uint64_t)(uint32_t)t * (2 * D)) & ~m) | (z_base & m);
+    };
+    // lane & 15 holds the index of row lane & 15 of the wave's step j
+    auto idx_v = [&](int j) -> int32_t { return j < nj ? sidx[kWvRows * (w + 4 * j) + (lane & 15)] : -1; };
+    auto issue = [&](int j, int32_t iv, int b) {
+        const uint32_t vb = wb_lds + b * Cfg::BUF;
+#pragma unroll
+        for (int r = 0; r < kWvRows; r++) {
+            const int32_t t = __builtin_amdgcn_readlane(iv, r);
+            dma16s(reinterpret_cast<const void *>(row_addr(t)), voff, vb + r * Cfg::VS);
+        }
+        if constexpr (D > 512) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int row = 8 * i + (lane >> 3);
+                const int32_t t = sidx[kWvRows * (w + 4 * j) + row];
+                const int piece = (lane & 7) ^ (row & 7);
+                dma16(reinterpret_cast<const uint8_t *>(row_addr(t)) + 1024 + 16 * piece, vb + Cfg::VBYTES + 1024 * i);
+            }
+        }
+    };
+
+    // The running max is only raised at a wave's first step, where nothing
+    // has been accumulated yet, to the step's max plus 16 (p <= 2^-16 then;
+    // fp32 keeps full relative precision far below that).  A later step
+    // whose max passes the reference by more than 8 raises it the same way
+    // and restarts the wave's rows from its first step, so the accumulators
+    // are never rescaled inside the loop.
+    f32x4 acc[32];
+    float m_ref = -INFINITY, l_part = 0.f;
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_part = 0.f;
+        bool restart = false;
+        if (nj > 0) issue(0, idx_v(0), 0);
+        if (nj > 1) issue(1, idx_v(1), 1);
+        // complete the query loads before the loop, whose vmcnt waits count
+        // DMA only (the first pass also waits for its first two steps here)
+#pragma unroll
+        for (int j = 0; j < Cfg::ND; j++) asm volatile("" ::"v"(qreg[j]));
+        for (int j = 0; j < nj; j++) {
+            const int32_t iv = idx_v(j);
+            if (j + 1 < nj)
+                wait_vm<Cfg::NDMA>();
+            else
+                wait_vm<0>();
+            const uint8_t *vb = wb + (j & 1) * Cfg::BUF;
+            const uint64_t okmask = __ballot(lane < kWvRows && iv >= 0);
+
+            // S^T of the step's 16 rows (lane: rows 4g .. 4g + 3 of head n),
+            // two independent accumulation chains
+            f32x4 s;
+            {
+                bf16x8 ra[Cfg::ND];
+#pragma unroll
+                for (int k = 0; k < Cfg::ND; k++) {
+                    const uint8_t *p0;
+                    if (D > 512 && k >= 16)
+                        p0 = vb + Cfg::VBYTES + n * 128 + 16 * ((4 * (k - 16) + g) ^ (n & 7));
+                    else
+                        p0 = vb + n * Cfg::VS + 64 * k + 16 * g;
+                    ra[k] = __builtin_bit_cast(bf16x8, *(const u32x4 *)p0);
+                }
+                // all reads in flight before the first product
+#pragma unroll
+                for (int k = 0; k < Cfg::ND; k++) asm volatile("" ::"v"(ra[k]));
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < Cfg::ND; k += 2) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[k], qreg[k], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[k + 1], qreg[k + 1], s1, 0, 0, 0);
+                }
+                s = s0 + s1;
+            }
+            float z[4];
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float v = ((okmask >> (4 * g + r)) & 1) ? s[r] * a.scale_log2 : -INFINITY;
+                z[r] = v;
+                cmax = fmaxf(cmax, v);
+            }
+            cmax = xor16_max(cmax);
+            cmax = xor32_max(cmax);
+            const bool need = cmax > m_ref + 8.f;
+            if (__any(need)) {
+                m_ref = need ? cmax + 16.f : m_ref;
+                if (j > 0) {
+                    restart = true;
+                    break;
+                }
+            }
+            bf16x8 pb;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float p = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+                l_part += p;
+                const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
+                const float lo = p - __uint_as_float(hb);
+                pb[r] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+                pb[4 + r] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(lo) >> 16));
+            }
+            // O^T += V^T P^T, 32 column blocks of 16
+            {
+                const uint8_t *v1 = vb + (4 * g + (n >> 2)) * Cfg::VS + 8 * (n & 3);
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                i16x4 t[32];
+#pragma unroll
+                for (int c = 0; c < 32; c++) t[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v1 + 32 * c));
+#pragma unroll
+                for (int c = 0; c < 32; c++) asm volatile("" ::"v"(t[c]));
+#pragma unroll
+                for (int c = 0; c < 32; c++) {
+                    const i16x8 tv = {t[c][0], t[c][1], t[c][2], t[c][3], t[c][0], t[c][1], t[c][2], t[c][3]};
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tv), pb, acc[c], 0, 0, 0);
+                }
+            }
+            // the buffer is free once its LDS reads have returned
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (j + 2 < nj) issue(j + 2, idx_v(j + 2), j & 1);
+        }
+        if (!restart) break;
+        // drain this pass's DMA before the buffers are filled again
+        wait_vm<0>();
+    }
+
+    // merge the four waves: each writes its (max, sum, O) to LDS; after one
+    // barrier every wave combines a quarter of the columns
+    const float l_w = xor32_sum(xor16_sum(l_part));
+    if (g == 0) {
+        smx[w][n] = m_ref;
+        ssum[w][n] = l_w;
+    }
+    __syncthreads();   // every wave is past its last LDS read of the row buffers
+    {
+        float *so = reinterpret_cast<float *>(lds) + w * 16 * Cfg::OS + n * Cfg::OS + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 32; cb++) *(f32x4 *)(so + 16 * cb) = acc[cb];
+    }
+    __syncthreads();
+    const float *sb = reinterpret_cast<const float *>(lds);
+    // lane: heads 4k + lane / 16 (k = 0..3), columns 128 w + 64 h + 4 (lane & 15) (h = 0, 1)
+    float fk[4][4], Lk[4], Mk[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int hh = 4 * k + (lane >> 4);
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) M = fmaxf(M, smx[ww][hh]);
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const float mw = smx[ww][hh];
+            fk[k][ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            L += ssum[ww][hh] * fk[k][ww];
+        }
+        Mk[k] = M;
+        Lk[k] = L;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int hh = 4 * k + (lane >> 4), hd = 16 * hg + hh;
+        const float L = Lk[k];
+        const bool bad = invalid || L == 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int col = 128 * w + 64 * h + 4 * (lane & 15);
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ww = 0; ww < 4; ww++) v += *(const f32x4 *)(sb + (ww * 16 + hh) * Cfg::OS + col) * fk[k][ww];
+            if (a.n_split == 1) {
+                const f32x4 o = bad ? f32x4{NAN, NAN, NAN, NAN} : v * (1.f / L);
+                *(f32x4 *)(a.out + ((size_t)q * kHeads + hd) * kLatent + col) = o;
+            } else {
+                const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + hd;
+                *(f32x4 *)(a.pacc + slot * kLatent + col) = v;
+            }
+        }
+        if (w == 0 && (lane & 15) == 0) {
+            if (a.n_split == 1) {
+                if (a.lse) a.lse[(size_t)q * kHeads + hd] = bad ? NAN : (Mk[k] + __log2f(L)) * 0.69314718055994531f;
+            } else {
+                const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + hd;
+                a.pml[2 * slot] = Mk[k];
+                a.pml[2 * slot + 1] = L;
+            }
+        }
+    }
+}
+
 // Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
 // thread four output columns.  Up to 16 splits are loaded in one round trip
 // and merged online (running max, rescaled sums).
@@ -1848,7 +2137,13 @@ hipError_t launch_select(const Args &a, hipStream_t st) {
 }
 
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between) {
-    if (a.attn_hs) {
+    if (a.attn_hs == 2) {
+        const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
+        if (a.D == 576)
+            hipLaunchKernelGGL(k_attend_wv<576>, dim3(4 * pairs8), dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_attend_wv<512>, dim3(4 * pairs8), dim3(256), 0, st, a);
+    } else if (a.attn_hs) {
         const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
         if (a.D == 576)
             hipLaunchKernelGGL(k_attend_hs<576>, dim3(4 * pairs8), dim3(512), 0, st, a);

@@ -17,6 +17,7 @@ constexpr int kMaxTopK = 4096;
 constexpr int kMaxChunks = 1024;  // top-k chunks per query (one per k_select thread)
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
 constexpr int kMaxSplitRows = 4096;  // selected rows per attention work-group
+constexpr int kWvMaxRows = 2048;     // the same for k_attend_wv
 
 // Everything a launch needs that depends on (geometry, n_q, max_nvis).
 struct Plan {
@@ -32,7 +33,7 @@ struct Plan {
     int32_t sel_max;              // top_k + kpool - 1
     int32_t split_rows;           // selected rows per attention work-group
     int32_t n_split;              // attention splits per query
-    int32_t attn_hs;              // 1: head-split attention kernel
+    int32_t attn_hs;              // attention kernel: 0 k_attend, 1 k_attend_hs, 2 k_attend_wv
     int32_t select_scan;          // 1: top-k in one kernel that scans the scores
     int32_t score_tile;           // key rows per score work-group
 
@@ -67,21 +68,29 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
     p.cand_cap = p.chunk / 4;     // a chunk's candidates beyond this are found again by k_select
 
-    // attention: up to 64 queries run head-split (k_attend_hs: a work-group
-    // per head group of 16, query and split), aiming at ~64 (query, split)
-    // pairs = 256 work-groups; more queries run k_attend (all 64 heads per
-    // work-group), aiming at ~128 work-groups.  Whole 32-row steps,
-    // 64..kMaxSplitRows rows per split.  Tuning overrides from the
-    // environment: DSA_ATTN_HS (0 or 1) picks the kernel, DSA_ATTN_PAIRS the
-    // (query, split) target.
-    p.attn_hs = n_q <= 64 ? 1 : 0;
-    if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) ? 1 : 0;
+    // attention kernels, by batch (decode at 8 x 128K: 17.5 vs 20.4 us for
+    // k_attend_wv vs k_attend_hs; at 64 queries 62 vs 94 us; at 1-2 queries
+    // k_attend_hs is ~1.3 us faster; beyond 64 queries, and for a prefill
+    // chunk, k_attend is as fast or faster):
+    //   1..3 queries  k_attend_hs (attn_hs 1): head group x query x split,
+    //                 8 waves sharing each 32-row step;
+    //   4..64         k_attend_wv (attn_hs 2): the same grid, 4 waves with
+    //                 private rows, merged once at the end;
+    //   more          k_attend (attn_hs 0): all 64 heads per work-group.
+    // The head-group kernels aim at ~64 (query, split) pairs = 256
+    // work-groups, k_attend at ~128 work-groups.  Whole 32-row steps,
+    // 64..kMaxSplitRows rows per split (kWvMaxRows for k_attend_wv).  Tuning
+    // overrides from the environment: DSA_ATTN_HS (0, 1 or 2) picks the
+    // kernel, DSA_ATTN_PAIRS the (query, split) target.
+    p.attn_hs = n_q < 4 ? 1 : n_q <= 64 ? 2 : 0;
+    if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) == 2 ? 2 : atoi(e) ? 1 : 0;
     int64_t ns = ((p.attn_hs ? 64 : 128) + n_q - 1) / n_q;
     if (const char *e = getenv("DSA_ATTN_PAIRS")) ns = (atoi(e) + n_q - 1) / n_q;
     int64_t sr = (p.sel_max + ns - 1) / ns;
     sr = (sr + 31) / 32 * 32;
     if (sr < 64) sr = 64;
     if (sr > kMaxSplitRows) sr = kMaxSplitRows;
+    if (p.attn_hs == 2 && sr > kWvMaxRows) sr = kWvMaxRows;
     p.split_rows = (int32_t)sr;
     p.n_split = (int32_t)((p.sel_max + sr - 1) / sr);
 

@@ -25,6 +25,10 @@ def setup_module():
     B.device_check()
 
 
+# DSA_ATTN_HS value that forces each attention kernel
+ATTN_KERNEL = {"wide": "0", "hs": "1", "wv": "2"}
+
+
 def geom(kpool=1, d_rope=64, top_k=2048):
     g = dict(I.GEOM_TOKEN)
     g.update(kpool=kpool, d_rope=d_rope, top_k=top_k)
@@ -144,11 +148,12 @@ def test_topk_bit_exact(kind, kpool, top_k, select, monkeypatch):
 
 @pytest.mark.parametrize("d_rope", [64, 0])
 @pytest.mark.parametrize("count", [1, 31, 32, 33, 100, 2048, 2051])
-@pytest.mark.parametrize("kernel", ["hs", "wide"])
+@pytest.mark.parametrize("kernel", ["hs", "wv", "wide"])
 def test_attend_matches_oracle(d_rope, count, kernel, monkeypatch):
-    """Both attention kernels (head-split, and all heads per work-group),
-    forced by the planner's override, against the oracle."""
-    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    """The three attention kernels (head-split, wave-private rows, and all
+    heads per work-group), forced by the planner's override, against the
+    oracle."""
+    monkeypatch.setenv("DSA_ATTN_HS", ATTN_KERNEL[kernel])
     log(f"attend d_rope={d_rope} count={count} kernel={kernel}")
     rng = np.random.default_rng(count * 7 + d_rope)
     g = geom(kpool=4 if d_rope == 0 else 1, d_rope=d_rope)
@@ -197,11 +202,11 @@ def _attend_case(d_rope, n_q, sel, cnt, T, seed):
 
 
 @pytest.mark.parametrize("d_rope", [64, 0])
-@pytest.mark.parametrize("kernel", ["hs", "wide"])
+@pytest.mark.parametrize("kernel", ["hs", "wv", "wide"])
 def test_attend_skips_invalid_rows_and_counts(d_rope, kernel, monkeypatch):
     """Entries outside [0, T) inside the count are skipped; a count outside
     [0, top_k + kpool - 1], or one that leaves no row, gives NaN."""
-    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    monkeypatch.setenv("DSA_ATTN_HS", ATTN_KERNEL[kernel])
     log(f"attend edge rows d_rope={d_rope} kernel={kernel}")
     rng = np.random.default_rng(91 + d_rope)
     T, n_q = 3000, 8
@@ -232,11 +237,55 @@ def test_attend_skips_invalid_rows_and_counts(d_rope, kernel, monkeypatch):
         assert np.isnan(out[j]).all() and np.isnan(lse[j]).all(), f"query {j} should be NaN"
 
 
-@pytest.mark.parametrize("kernel", ["hs", "wide"])
+@pytest.mark.parametrize("pairs", [None, "4"])
+@pytest.mark.parametrize("d_rope", [64, 0])
+@pytest.mark.parametrize("kernel", ["hs", "wv", "wide"])
+def test_attend_rising_scores(kernel, d_rope, pairs, monkeypatch):
+    """Scores that rise by ~11.5 log2 units from one 16-row step of a wave
+    to its next: every kernel must move its softmax reference many times
+    (k_attend_wv restarts its rows each time).  The scores are integers
+    (queries 1 on the first 64 dimensions, cache entries integer there), so
+    they are exact in any summation order; with pairs = 4 every query is one
+    2048-row split."""
+    monkeypatch.setenv("DSA_ATTN_HS", ATTN_KERNEL[kernel])
+    if pairs:
+        monkeypatch.setenv("DSA_ATTN_PAIRS", pairs)
+    log(f"attend rising scores kernel={kernel} d_rope={d_rope} pairs={pairs}")
+    rng = np.random.default_rng(41 + d_rope)
+    g = geom(kpool=4 if d_rope == 0 else 1, d_rope=d_rope)
+    D = 512 + d_rope
+    T, n_q = 6000, 4
+    sel_ld = g["top_k"] + g["kpool"] - 1
+    cache = rng.standard_normal((2, T, D)).astype(np.float32)
+    q = np.zeros((n_q, 64, D), np.float32)
+    q[:, :, :64] = 1.0
+    q_seq = (np.arange(n_q) % 2).astype(np.int32)
+    sel = np.full((n_q, sel_ld), -1, np.int32)
+    cnt = np.full(n_q, 2048, np.int32)
+    for j in range(n_q):
+        rows = np.sort(rng.choice(T, 2048, replace=False))
+        sel[j, :2048] = rows
+        # the p-th selected row scores 64 * 2 * (p // 64)
+        cache[q_seq[j], rows, :64] = (2 * (np.arange(2048) // 64))[:, None]
+    cache = I.f32_to_bf16_bits(cache)
+    q = I.f32_to_bf16_bits(q)
+    out_ref, lse_ref = O.mla_attend(q_seq, 512, d_rope, 1 / 16, q, cache, sel, cnt)
+    dev = "cuda"
+    b = B.batch(torch.from_numpy(q_seq).to(dev), torch.full((n_q,), T, dtype=torch.int32, device=dev), T, 2)
+    ws = B.new_workspace(g, n_q, T)
+    out = torch.full((n_q, 64, 512), float("nan"), device=dev)
+    lse = torch.full((n_q, 64), float("nan"), device=dev)
+    B.mla_attend(g, b, torch.from_numpy(q).to(dev), torch.from_numpy(cache).to(dev), T,
+                 torch.from_numpy(sel).to(dev), sel_ld, torch.from_numpy(cnt).to(dev), out, lse, ws)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), out_ref, lse_ref, f"rising D={D}")
+
+
+@pytest.mark.parametrize("kernel", ["hs", "wv", "wide"])
 def test_attend_single_split_path(kernel, monkeypatch):
     """Many queries: every query is one work-group (or four head groups)
     that writes its output directly (no split merge)."""
-    monkeypatch.setenv("DSA_ATTN_HS", "1" if kernel == "hs" else "0")
+    monkeypatch.setenv("DSA_ATTN_HS", ATTN_KERNEL[kernel])
     log(f"attend single split kernel={kernel}")
     rng = np.random.default_rng(17)
     T, n_q = 2500, 300
