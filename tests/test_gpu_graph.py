@@ -1,0 +1,68 @@
+"""The fused step captured in a HIP graph (through torch.cuda.CUDAGraph) and
+replayed several times, with eager work and synchronisation between the
+replays: every replay must reproduce the eager call bit for bit.  The
+library allocates nothing and records no memset, so its launches are
+capturable as they stand."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from gpu_common import log, gpu_arch
+
+pytestmark = pytest.mark.gpu
+
+from deepseek_sparse_attention_amd import binding as B            # noqa: E402
+from deepseek_sparse_attention_amd import inputs as I             # noqa: E402
+from deepseek_sparse_attention_amd.workload import DeviceWorkload  # noqa: E402
+
+
+def setup_module():
+    assert gpu_arch().startswith("gfx950")
+    B.device_check()
+
+
+# name, geometry, n_seq, T, q_seq, q_nvis: a batch that takes the chunked
+# top-k (rows > 16,384), the wave-private attention with splits and the
+# merge, plus a dense query and an invalid one
+CASES = [
+    ("tok_chunked", dict(I.GEOM_TOKEN), 4, 40000, [0, 1, 2, 3, 0], [40000, 30001, 20480, 1500, 0]),
+    ("pool", dict(I.GEOM_TOKEN, kpool=4, d_rope=0), 2, 90001, [0, 1, 1], [90001, 70003, 2051]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_captured_step_replays_match_eager(case):
+    name, g, n_seq, T, q_seq, q_nvis = case
+    log(f"graph {name}")
+    w = I.make_workload(name, 300, g, n_seq, T, q_seq, q_nvis)
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dw.sel, dw.sel_count, dw.out, dw.lse)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dw.decode_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dw.decode_step()
+    torch.cuda.synchronize()
+
+    for k in range(4):
+        # eager work between the replays: poison every output
+        dw.sel.fill_(-7)
+        dw.sel_count.fill_(-7)
+        dw.out.fill_(float("nan"))
+        dw.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((dw.sel, dw.sel_count, dw.out, dw.lse), ref, ("sel", "count", "out", "lse")):
+            assert torch.equal(got, want) or (what in ("out", "lse") and torch.equal(got.nan_to_num(7.0),
+                                                                                  want.nan_to_num(7.0))), \
+                f"{name}: replay {k}: {what} differs from the eager call"
+    del graph
