@@ -78,13 +78,16 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     //                 private rows, merged once at the end;
     //   more          k_attend (attn_hs 0): all 64 heads per work-group.
     // The head-group kernels aim at ~64 (query, split) pairs = 256
-    // work-groups, k_attend at ~128 work-groups.  Whole 32-row steps,
+    // work-groups, k_attend at up to 256 work-groups.  Whole 32-row steps,
     // 64..kMaxSplitRows rows per split (kWvMaxRows for k_attend_wv).  Tuning
     // overrides from the environment: DSA_ATTN_HS (0, 1 or 2) picks the
     // kernel, DSA_ATTN_PAIRS the (query, split) target.
     p.attn_hs = n_q < 4 ? 1 : n_q <= 64 ? 2 : 0;
     if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) == 2 ? 2 : atoi(e) ? 1 : 0;
-    int64_t ns = ((p.attn_hs ? 64 : 128) + n_q - 1) / n_q;
+    // k_attend runs one work-group per CU (143 KiB of LDS): as many splits as
+    // keep the grid within one round of 256 work-groups (8 x 128K at 128
+    // queries: 2 splits, 100 us for attention + merge against 144 us with 1)
+    int64_t ns = p.attn_hs ? (64 + n_q - 1) / n_q : (n_q < 256 ? 256 / n_q : 1);
     if (const char *e = getenv("DSA_ATTN_PAIRS")) ns = (atoi(e) + n_q - 1) / n_q;
     int64_t sr = (p.sel_max + ns - 1) / ns;
     sr = (sr + 31) / 32 * 32;
