@@ -103,7 +103,19 @@ def cpu_baseline(w, budget_s: float):
             break
     return {"value": round(done * w.n_q / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} full step(s) of the same workload ({done * w.n_q} queries), "
-                      f"{el:.1f} s wall on {threads} OpenMP threads"}
+                      f"{el:.1f} s wall on {threads} OpenMP threads of {cpu_model()}"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo, or "unknown CPU"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main() -> int:
