@@ -106,6 +106,29 @@ def cpu_baseline(w, budget_s: float):
                       f"{el:.1f} s wall on {threads} OpenMP threads of {cpu_model()}"}
 
 
+def stream_read_rate(gib: int = 1, reps: int = 20) -> dict:
+    """The plainest streaming read of HBM on this device (the library's
+    non-temporal grid-stride probe over a buffer of `gib` GiB, which no cache
+    holds): the practical read roof beside the published 8 TB/s."""
+    import torch
+    from deepseek_sparse_attention_amd import binding as B
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        B.stream_read(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        B.stream_read(buf, sink)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    gbps = buf.numel() / (us * 1e-6) / 1e9
+    del buf
+    return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": gib << 30,
+            "us": round(us, 2)}
+
+
 def cpu_model() -> str:
     """The host CPU's model name from /proc/cpuinfo, or "unknown CPU"."""
     try:
@@ -244,6 +267,8 @@ def main() -> int:
         "kernels_us": {k: round(v, 2) for k, v in per.items()},
         "roofline": roof,
     }
+    if not prefill:
+        res["stream_read"] = stream_read_rate()
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -29,7 +29,7 @@ class Batch(ctypes.Structure):
 
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
            "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_index_prepare",
-           "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events")
+           "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events", "dsa_stream_read")
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -53,6 +53,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_device_check": (ctypes.c_int, []),
         "dsa_set_timing_events": (ctypes.c_int, [P, i32]),
+        "dsa_stream_read": (ctypes.c_int, [P, sz, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -215,6 +216,16 @@ def index_prepare(geom: dict, b: Batch, q_in, q_out, k_seq, k_pos, k_in, idx_k, 
     _check(_lib.dsa_index_prepare(ctypes.byref(geometry(geom)), ctypes.byref(b), float(rope_base), _ptr(q_in),
                                   _ptr(q_out), n_new, _ptr(k_seq), _ptr(k_pos), _ptr(k_in), _ptr(idx_k),
                                   int(key_seq_stride), _stream(stream)), "dsa_index_prepare")
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """Bandwidth probe: reads all of buf (a contiguous cuda tensor whose byte
+    size is a multiple of 16) with streaming loads; sink: an int32 cuda
+    tensor of at least one element."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.dtype != torch.int32:
+        raise TypeError("buf: a contiguous cuda tensor; sink: an int32 cuda tensor")
+    _check(_lib.dsa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "dsa_stream_read")
 
 
 def set_timing_events(events) -> None:

@@ -24,6 +24,7 @@ hipError_t launch_hist(const Args &a, hipStream_t st);
 hipError_t launch_filter(const Args &a, hipStream_t st);
 hipError_t launch_select(const Args &a, hipStream_t st);
 hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
 hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st);
 hipError_t launch_project(const AbsorbArgs &a, hipStream_t st);
@@ -196,6 +197,15 @@ int dsa_set_timing_events(hipEvent_t *events, int32_t n_events) {
     g_events = (events && n_events > 0) ? events : nullptr;
     g_n_events = g_events ? n_events : 0;
     return DSA_OK;
+}
+
+int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        if (!buf || !aligned16(buf) || bytes == 0 || bytes % 16 != 0 || !sink)
+            return fail(DSA_ERR_ARG, "stream_read: buffer NULL, misaligned or empty, or sink NULL");
+        return launched(dsa::launch_stream_read(buf, bytes, sink, stream), "stream_read");
+    });
 }
 
 int dsa_device_check(void) {

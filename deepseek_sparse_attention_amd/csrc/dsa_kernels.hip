@@ -202,6 +202,17 @@ __global__ void k_fill_zero(uint32_t *p, size_t n_words) {
     for (; i < n_words; i += stride) p[i] = 0u;
 }
 
+// Streaming-read probe: non-temporal 16-byte loads over the whole buffer in
+// a grid-stride loop (consecutive threads, consecutive 16 bytes).
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4 *p, size_t n, uint32_t *sink) {
+    uint32_t x = 0;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const u32x4 t = __builtin_nontemporal_load(p + i);
+        x ^= t[0] ^ t[1] ^ t[2] ^ t[3];
+    }
+    if (x == 0x9e3779b9u) *sink = x;
+}
+
 // ---------------------------------------------------------------- scores
 // max(x, 0) in one integer max: a float with its sign bit set is a negative
 // int32, so every negative x (and -0) becomes +0 and every positive x stays.
@@ -2125,6 +2136,12 @@ hipError_t launch_hist(const Args &a, hipStream_t st) {
 
 hipError_t launch_filter(const Args &a, hipStream_t st) {
     hipLaunchKernelGGL(k_filter, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
+    // 2,048 work-groups of 256 threads: 8 per CU, each wave a few loads in flight
+    hipLaunchKernelGGL(k_stream_read, dim3(2048), dim3(256), 0, st, static_cast<const u32x4 *>(buf), bytes / 16, sink);
     return hipGetLastError();
 }
 

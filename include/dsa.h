@@ -270,6 +270,15 @@ int dsa_index_prepare(const dsa_geometry *geom, const dsa_batch *batch, double r
  * Returns DSA_OK. */
 int dsa_set_timing_events(hipEvent_t *events, int32_t n_events);
 
+/* Bandwidth probe for benchmarks: reads bytes (a multiple of 16) from the
+ * 16-byte aligned device buffer buf with non-temporal 16-byte loads in a
+ * grid-stride loop, the plainest streaming read of HBM, so that a benchmark
+ * can report the read bandwidth the device sustains beside its published
+ * peak.  *sink (device) is written only if the loaded words xor to an
+ * impossible pattern, which keeps the loads alive.  DSA_ERR_ARG for a NULL,
+ * misaligned or empty buffer. */
+int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *dsa_status_str(int status);
 

@@ -66,3 +66,18 @@ def test_captured_step_replays_match_eager(case):
                                                                                   want.nan_to_num(7.0))), \
                 f"{name}: replay {k}: {what} differs from the eager call"
     del graph
+
+
+def test_stream_read_probe():
+    """The bandwidth probe reads a buffer without writing its sink (the
+    words of a constant buffer xor to zero), and refuses a size that is not
+    a multiple of 16 bytes or a misaligned buffer."""
+    buf = torch.full((1 << 20,), 3, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    with pytest.raises(B.DSAError):
+        B.stream_read(buf[:100], sink)
+    with pytest.raises(B.DSAError):
+        B.stream_read(buf[1:1 + 4096], sink)
