@@ -214,9 +214,9 @@ def main() -> int:
     print(f"[bench] {ms_step * 1e3:.1f} us/step, wall {wall * 1e3 / args.steps:.1f} us/step", file=sys.stderr,
           flush=True)
 
-    # ---- per-kernel durations: events recorded by the library around each
-    # kernel of the same fused step, over a second pass of the same length
-    n_k = len(KERNELS) + 1
+    # ---- per-kernel durations: each kernel of the same fused step launched
+    # with its own start and stop events, over a second pass
+    n_k = 2 * len(KERNELS)
     n_rep = min(args.steps, 100)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k)] for _ in range(n_rep)]
     for row in evs:
@@ -232,7 +232,7 @@ def main() -> int:
     per = {k: 0.0 for k in names}
     for row in evs:
         for j, k in enumerate(names):
-            per[k] += row[j].elapsed_time(row[j + 1]) * 1e3 / n_rep
+            per[k] += row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3 / n_rep
     score_us = per["score"]
     prefill = w.n_seq == 1 and w.n_q > 1
     if prefill:

@@ -230,7 +230,8 @@ def stream_read(buf, sink, stream=None) -> None:
 
 def set_timing_events(events) -> None:
     """events: a list of torch.cuda.Event(enable_timing=True), or None to stop.
-    The library records them around each kernel of dsa_decode_step."""
+    dsa_decode_step launches its i-th kernel with events[2i] and
+    events[2i + 1] as that kernel's own start and stop marks."""
     if not events:
         _lib.dsa_set_timing_events(None, 0)
         set_timing_events._keep = None

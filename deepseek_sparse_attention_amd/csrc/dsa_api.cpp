@@ -8,7 +8,6 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-#include <functional>
 #include <mutex>
 #include <string>
 
@@ -19,11 +18,12 @@
 
 namespace dsa {
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
-hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st);
+hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
 hipError_t launch_hist(const Args &a, hipStream_t st);
-hipError_t launch_filter(const Args &a, hipStream_t st);
-hipError_t launch_select(const Args &a, hipStream_t st);
-hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between = {});
+hipError_t launch_filter(const Args &a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_select(const Args &a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev = nullptr);
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
 hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st);
@@ -37,15 +37,8 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t *g_events = nullptr;
 thread_local int32_t g_n_events = 0;
 
-// Records the next timing event of this call, if instrumentation is on.
-struct Timer {
-    hipStream_t st;
-    int32_t next = 0;
-    explicit Timer(hipStream_t s) : st(s) { tick(); }
-    void tick() {
-        if (g_events && next < g_n_events) (void)hipEventRecord(g_events[next++], st);
-    }
-};
+// Timing event i of this call, or NULL when instrumentation is off.
+hipEvent_t timing_event(int32_t i) { return g_events && i < g_n_events ? g_events[i] : nullptr; }
 
 int fail(int status, const std::string &msg) {
     g_last_error = msg;
@@ -354,15 +347,17 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
         a.out = out;
         a.lse = lse;
         a.fused = 1;
-        Timer tm(stream);
-        DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream), "score"));
-        tm.tick();
-        if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
-        tm.tick();
-        DSA_TRY(launched(dsa::launch_select(a, stream), "select"));
-        tm.tick();
-        DSA_TRY(launched(dsa::launch_attend(a, stream, [&] { tm.tick(); }), "attend"));
-        tm.tick();
+        hipEvent_t ev[10];
+        for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
+        DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream, ev[0], ev[1]), "score"));
+        if (!a.select_scan) {
+            DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
+        } else {
+            for (int i = 2; i < 4; i++)
+                if (ev[i]) (void)hipEventRecord(ev[i], stream);
+        }
+        DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
+        DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
         return (int)DSA_OK;
     });
 }

@@ -29,10 +29,10 @@
 // ds_read_b64_tr_b16 and P split into two bf16 halves (hi + lo) so that P
 // carries ~16 mantissa bits; split partials are merged by an LSE reduction.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <functional>
 #include <type_traits>
 
 #include "dsa_args.h"
@@ -2096,6 +2096,17 @@ __global__ __launch_bounds__(256) void k_project(AbsorbArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
+// A launch that, given events, takes them as its own start and stop marks
+// (hipExtLaunchKernel stamps them from the dispatch itself, so their
+// interval is the kernel's execution time, as a kernel trace reports it).
+#define DSA_LAUNCH(EV0, EV1, KERNEL, GRID, BLOCK, ST, ...)                                    \
+    do {                                                                                      \
+        if ((EV0) || (EV1))                                                                   \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, ST, EV0, EV1, 0, __VA_ARGS__);      \
+        else                                                                                  \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, ST, __VA_ARGS__);                      \
+    } while (0)
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
     const size_t words = bytes / 4;
     if (words == 0) return hipSuccess;
@@ -2106,27 +2117,28 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
 }
 
 template <bool F16>
-hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st) {
+hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.prefill) {
         const unsigned ranges = (unsigned)((max_rows + kPfRange - 1) / kPfRange);
         const unsigned runs = (unsigned)((a.n_q + a.pf_run - 1) / a.pf_run);
         const unsigned per = (unsigned)((a.pf_run + kPfQ - 1) / kPfQ);
-        hipLaunchKernelGGL(k_score_prefill<F16>, dim3(ranges, runs * per), dim3(kPfWaves * 64), 0, st, a);
+        DSA_LAUNCH(ev0, nullptr, k_score_prefill<F16>, dim3(ranges, runs * per), dim3(kPfWaves * 64), st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // in prefill mode k_score only picks up queries outside their block's
     // sequence: one work-group per query, striding over the tiles
     if (a.prefill)
-        hipLaunchKernelGGL((k_score<true, F16>), dim3(1, a.n_q), dim3(256), 0, st, a);
+        DSA_LAUNCH(nullptr, ev1, (k_score<true, F16>), dim3(1, a.n_q), dim3(256), st, a);
     else
-        hipLaunchKernelGGL((k_score<false, F16>),
-                           dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(256), 0, st, a);
+        DSA_LAUNCH(ev0, ev1, (k_score<false, F16>),
+                   dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(256), st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st) {
-    return a.idx_f16 ? launch_score_fmt<true>(a, max_rows, st) : launch_score_fmt<false>(a, max_rows, st);
+hipError_t launch_score(const Args &a, int64_t max_rows, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    return a.idx_f16 ? launch_score_fmt<true>(a, max_rows, st, ev0, ev1)
+                     : launch_score_fmt<false>(a, max_rows, st, ev0, ev1);
 }
 
 hipError_t launch_hist(const Args &a, hipStream_t st) {
@@ -2134,8 +2146,8 @@ hipError_t launch_hist(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_filter(const Args &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_filter, dim3(a.n_chunks, a.n_q), dim3(256), 0, st, a);
+hipError_t launch_filter(const Args &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    DSA_LAUNCH(ev0, ev1, k_filter, dim3(a.n_chunks, a.n_q), dim3(256), st, a);
     return hipGetLastError();
 }
 
@@ -2145,36 +2157,43 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hip
     return hipGetLastError();
 }
 
-hipError_t launch_select(const Args &a, hipStream_t st) {
+hipError_t launch_select(const Args &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.select_scan)
-        hipLaunchKernelGGL(k_select<true>, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
+        DSA_LAUNCH(ev0, ev1, k_select<true>, dim3(a.n_q), dim3(kSelThreads), st, a);
     else
-        hipLaunchKernelGGL(k_select<false>, dim3(a.n_q), dim3(kSelThreads), 0, st, a);
+        DSA_LAUNCH(ev0, ev1, k_select<false>, dim3(a.n_q), dim3(kSelThreads), st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attend(const Args &a, hipStream_t st, const std::function<void()> &between) {
+// The attention kernel takes ev[0] and ev[1], the split merge ev[2] and
+// ev[3] (recorded back to back when there is no merge); ev may be NULL.
+hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev) {
+    const hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     if (a.attn_hs == 2) {
         const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
         if (a.D == 576)
-            hipLaunchKernelGGL(k_attend_wv<576>, dim3(4 * pairs8), dim3(256), 0, st, a);
+            DSA_LAUNCH(e0, e1, k_attend_wv<576>, dim3(4 * pairs8), dim3(256), st, a);
         else
-            hipLaunchKernelGGL(k_attend_wv<512>, dim3(4 * pairs8), dim3(256), 0, st, a);
+            DSA_LAUNCH(e0, e1, k_attend_wv<512>, dim3(4 * pairs8), dim3(256), st, a);
     } else if (a.attn_hs) {
         const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
         if (a.D == 576)
-            hipLaunchKernelGGL(k_attend_hs<576>, dim3(4 * pairs8), dim3(512), 0, st, a);
+            DSA_LAUNCH(e0, e1, k_attend_hs<576>, dim3(4 * pairs8), dim3(512), st, a);
         else
-            hipLaunchKernelGGL(k_attend_hs<512>, dim3(4 * pairs8), dim3(512), 0, st, a);
+            DSA_LAUNCH(e0, e1, k_attend_hs<512>, dim3(4 * pairs8), dim3(512), st, a);
     } else if (a.D == 576) {
-        hipLaunchKernelGGL(k_attend<576>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
+        DSA_LAUNCH(e0, e1, k_attend<576>, dim3(a.n_split, a.n_q), dim3(512), st, a);
     } else {
-        hipLaunchKernelGGL(k_attend<512>, dim3(a.n_split, a.n_q), dim3(512), 0, st, a);
+        DSA_LAUNCH(e0, e1, k_attend<512>, dim3(a.n_split, a.n_q), dim3(512), st, a);
     }
     hipError_t e = hipGetLastError();
-    if (between) between();
-    if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(k_reduce, dim3(kHeads, a.n_q), dim3(128), 0, st, a);
+    if (e != hipSuccess) return e;
+    if (a.n_split == 1) {
+        if (ev && ev[2]) (void)hipEventRecord(ev[2], st);
+        if (ev && ev[3]) (void)hipEventRecord(ev[3], st);
+        return e;
+    }
+    DSA_LAUNCH(ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, k_reduce, dim3(kHeads, a.n_q), dim3(128), st, a);
     return hipGetLastError();
 }
 

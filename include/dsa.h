@@ -262,12 +262,15 @@ int dsa_index_prepare(const dsa_geometry *geom, const dsa_batch *batch, double r
                       dsa_bf16 *idx_k, int64_t key_seq_stride, hipStream_t stream);
 
 /* Instrumentation for benchmarks.  With events set (n_events > 0), each
- * dsa_decode_step call on this thread records events[0] on its stream before
- * its first kernel and events[i + 1] after its i-th kernel (as many as fit),
- * so elapsed(events[i], events[i + 1]) brackets kernel i.  Kernel order:
- * score, filter, select, attend, split merge (six events in all; the merge
- * interval is empty when the attention is not split).  Pass NULL/0 to stop.
- * Returns DSA_OK. */
+ * dsa_decode_step call on this thread launches its i-th kernel with
+ * events[2 i] and events[2 i + 1] as the kernel's own start and stop marks
+ * (hipExtLaunchKernel: the marks come from the dispatch, so
+ * elapsed(events[2 i], events[2 i + 1]) is the kernel's execution time, as a
+ * kernel trace reports it), as many as fit.  Kernel order: score, filter,
+ * select, attend, split merge (ten events in all); a kernel the call does
+ * not run (the filter of a one-kernel top-k, the merge of an unsplit
+ * attention) has its two events recorded back to back.  Pass NULL/0 to
+ * stop.  Returns DSA_OK. */
 int dsa_set_timing_events(hipEvent_t *events, int32_t n_events);
 
 /* Bandwidth probe for benchmarks: reads bytes (a multiple of 16) from the
