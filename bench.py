@@ -348,8 +348,9 @@ def run_absorb(args) -> int:
     """Absorption GEMMs (absorb the key up-projection into the query, project
     the attention output through the value up-projection), 64 heads, bf16
     weights [64][256][512] each.  Timed for a decode batch of 8 queries (the
-    32 MiB of weights dominate: HBM-bound) and a 512-query prefill chunk
-    (MFMA-bound); 4 weight replicas rotated."""
+    32 MiB of weights dominate) and a 512-query prefill chunk; both are
+    HBM-bound (the chunk does about 115 and 150 flop per byte, under the
+    ~312 flop/B ridge of 2.5 PFLOP/s over 8 TB/s); 4 weight replicas rotated."""
     import torch
     from deepseek_sparse_attention_amd import binding as B
 
@@ -370,13 +371,24 @@ def run_absorb(args) -> int:
             B.absorb_query(qn, qr, wk[i % R], qa)
             B.project_output(o, wv[i % R], ctx)
         torch.cuda.synchronize()
+        # each kernel's `steps` launches back to back (weights rotated),
+        # captured in a HIP graph so that the host's per-call cost does not
+        # stretch the few-microsecond decode launches
+        graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+        with torch.cuda.graph(graphs[0]):
+            for i in range(args.steps):
+                B.absorb_query(qn, qr, wk[i % R], qa)
+        with torch.cuda.graph(graphs[1]):
+            for i in range(args.steps):
+                B.project_output(o, wv[i % R], ctx)
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record()
-        for i in range(args.steps):                      # back to back, weights rotated
-            B.absorb_query(qn, qr, wk[i % R], qa)
+        graphs[0].replay()
         ev[1].record()
-        for i in range(args.steps):
-            B.project_output(o, wv[i % R], ctx)
+        graphs[1].replay()
         ev[2].record()
         torch.cuda.synchronize()
         ta = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps

@@ -37,6 +37,10 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t *g_events = nullptr;
 thread_local int32_t g_n_events = 0;
 
+// Queries per absorption call: keeps the 1-D grid (512 work-groups of 256
+// threads per 64 queries) under 2^32 work-items.
+constexpr int32_t kMaxAbsorbQueries = 1 << 20;
+
 // Timing event i of this call, or NULL when instrumentation is off.
 hipEvent_t timing_event(int32_t i) { return g_events && i < g_n_events ? g_events[i] : nullptr; }
 
@@ -397,6 +401,7 @@ int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const 
     return guarded([&] {
         DSA_TRY(check_device());
         if (n_q < 1) return fail(DSA_ERR_ARG, "n_q < 1");
+        if (n_q > kMaxAbsorbQueries) return fail(DSA_ERR_UNSUPPORTED, "n_q > 2^20");
         if (d_rope != 0 && d_rope != 64) return fail(DSA_ERR_UNSUPPORTED, "d_rope must be 0 or 64");
         if (!q_nope || !w_uk || !q_abs || (d_rope && !q_rope)) return fail(DSA_ERR_ARG, "NULL pointer");
         if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_abs) || (d_rope && !aligned16(q_rope)))
@@ -417,6 +422,7 @@ int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float 
     return guarded([&] {
         DSA_TRY(check_device());
         if (n_q < 1) return fail(DSA_ERR_ARG, "n_q < 1");
+        if (n_q > kMaxAbsorbQueries) return fail(DSA_ERR_UNSUPPORTED, "n_q > 2^20");
         if (!o || !w_uv || !ctx) return fail(DSA_ERR_ARG, "NULL pointer");
         if (!aligned16(o) || !aligned16(w_uv) || !aligned16(ctx))
             return fail(DSA_ERR_ARG, "pointers must be 16-byte aligned");

@@ -1975,33 +1975,54 @@ __global__ __launch_bounds__(256) void k_pool_append(PoolArgs a) {
 //   q_abs[m][h][n] = bf16( sum_k q_nope[m][h][k] W_UK[h][k][n] ),  n < 512, then q_rope
 //   ctx[m][h][i]   = sum_j o[m][h][j] W_UV[h][i][j],                i < 256
 // Both as C^T = W' X^T on MFMA 16x16x32 bf16: A = 16 weight rows (output
-// features) x 32 k, held in registers for all queries; B = 16 queries x 32 k,
-// loaded directly (k contiguous); D lands as 4 consecutive features of one
-// query per lane.
+// features) x 32 k; B = 16 queries x 32 k, loaded directly (k contiguous);
+// D lands as 4 consecutive features of one query per lane.  A work-group
+// owns 64 output features of one head (four 16-feature tiles) and a chunk of
+// up to kAbsorbRows queries.  With four or more 16-query blocks, wave w takes
+// blocks w, w + 4, ... and all four tiles, so every query row is read once
+// per work-group; with fewer, wave w takes tile w of every block.
 constexpr int kNope = 256;   // q_nope width per head
 constexpr int kVdim = 256;   // value width per head (output of the projection)
-constexpr int kAbsorbRows = 64;  // queries per work-group (grid z spreads the rest)
+constexpr int kAbsorbRows = 256;  // queries per work-group (the grid spreads the rest)
 
-// grid (8 slices of 64 latent dimensions, 64 heads), 256 threads: wave w
-// computes latent dimensions n0 + 16w .. n0 + 16w + 15.  W_UK[h] rows are
-// latent-contiguous, so the slice is staged in LDS (row stride 144 B) and
-// read transposed with ds_read_b64_tr_b16.
+// Work-group -> (output slice, head, query chunk) over a 1-D grid of
+// S x 64 x C work-groups.  Work-groups are dealt to the eight XCDs in turn,
+// so XCD x takes heads x, x + 8, ..., and the S x C work-groups of one head
+// run side by side there and share the head's weights and activations in
+// that XCD's L2 instead of each fetching them from HBM.
+struct AbsTile {
+    int slice, head, chunk;
+};
+__device__ __forceinline__ AbsTile abs_tile(int S, int C) {
+    const int L = blockIdx.x, x = L & 7, j = L >> 3, per = S * C;
+    const int hi = j / per, rem = j - hi * per;
+    return {rem % S, x + 8 * hi, rem / S};
+}
+
+// grid 8 slices of 64 latent dimensions x 64 heads x query chunks (abs_tile),
+// 256 threads.  W_UK[h] rows are latent-contiguous, so the slice is staged in
+// LDS (row stride 144 B) and read transposed with ds_read_b64_tr_b16 for
+// every query block.
 __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
     constexpr int RS = 144;
+    constexpr int KS = kNope / 32;
     __shared__ __attribute__((aligned(16))) uint8_t wl[kNope * RS];
-    const int h = blockIdx.y, n0 = 64 * blockIdx.x;
+    const AbsTile tl = abs_tile(kLatent / 64, (a.n_q + kAbsorbRows - 1) / kAbsorbRows);
+    const int h = tl.head, n0 = 64 * tl.slice;
     const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
-    const int m_begin = kAbsorbRows * blockIdx.z;
+    const int m_begin = kAbsorbRows * tl.chunk;
     const int m_end = m_begin + kAbsorbRows < a.n_q ? m_begin + kAbsorbRows : a.n_q;
+    const bool by_tile = m_end - m_begin <= 48;        // fewer than four 16-query blocks
+    const int mb0 = by_tile ? m_begin : m_begin + 16 * w, mstep = by_tile ? 16 : 64;
     // this lane's query row of a 16-query block, k = 32 ks + 8 g .. + 7
-    auto load_q = [&](int m0, bf16x8 (&bq)[kNope / 32]) {
+    auto load_q = [&](int m0, bf16x8 (&bq)[KS]) {
         const int m = m0 + n;
         const uint16_t *qn = a.q_nope + ((size_t)(m < m_end ? m : m_begin) * kHeads + h) * kNope + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < kNope / 32; ks++) bq[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qn + 32 * ks));
+        for (int ks = 0; ks < KS; ks++) bq[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qn + 32 * ks));
     };
-    bf16x8 bq[kNope / 32];
-    load_q(m_begin, bq);                      // in flight while the weights are staged
+    bf16x8 bq[KS];
+    if (mb0 < m_end) load_q(mb0, bq);          // in flight while the weights are staged
     {
         const uint8_t *W = reinterpret_cast<const uint8_t *>(a.w_uk + (size_t)h * kNope * kLatent + n0);
 #pragma unroll
@@ -2011,43 +2032,47 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
         }
     }
     __syncthreads();
-    bf16x8 wa[kNope / 32];
-    {
+    // A operand of tile t, k-step ks, read transposed from the staged slice
+    auto wtile = [&](int t, int ks) {
         const int r_in = n >> 2, c_in = n & 3;
-#pragma unroll
-        for (int ks = 0; ks < kNope / 32; ks++) {
-            const uint8_t *p1 = wl + (32 * ks + 8 * g + r_in) * RS + (16 * w + 4 * c_in) * 2;
-            const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
-            const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1 + 4 * RS));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            const i16x8 tv = {t1[0], t1[1], t1[2], t1[3], t2[0], t2[1], t2[2], t2[3]};
-            wa[ks] = __builtin_bit_cast(bf16x8, tv);
-        }
-    }
+        const uint8_t *p1 = wl + (32 * ks + 8 * g + r_in) * RS + (16 * t + 4 * c_in) * 2;
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
+        const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1 + 4 * RS));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 tv = {t1[0], t1[1], t1[2], t1[3], t2[0], t2[1], t2[2], t2[3]};
+        return __builtin_bit_cast(bf16x8, tv);
+    };
     const int D = kLatent + a.d_rope;
-    auto block = [&](int m0, const bf16x8 (&b)[kNope / 32]) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kNope / 32; ks++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b[ks], acc, 0, 0, 0);
+    auto block = [&](int m0, const bf16x8 (&b)[KS]) {
         const int m = m0 + n;
-        if (m < m_end) {
-            const uint32_t lo = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
-            const uint32_t hi = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
-            uint16_t *dst = a.q_abs + ((size_t)m * kHeads + h) * D + n0 + 16 * w + 4 * g;
-            *(uint2 *)dst = make_uint2(lo, hi);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            if (by_tile && t != w) continue;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wtile(t, ks), b[ks], acc, 0, 0, 0);
+            if (m < m_end) {
+                const uint32_t lo = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
+                const uint32_t hi = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
+                uint16_t *dst = a.q_abs + ((size_t)m * kHeads + h) * D + n0 + 16 * t + 4 * g;
+                *(uint2 *)dst = make_uint2(lo, hi);
+            }
         }
     };
     // two query blocks per trip, each one's operands loaded a block ahead
-    bf16x8 bq2[kNope / 32];
-    for (int m0 = m_begin; m0 < m_end; m0 += 32) {
-        if (m0 + 16 < m_end) load_q(m0 + 16, bq2);
+    bf16x8 bq2[KS];
+    for (int m0 = mb0; m0 < m_end; m0 += 2 * mstep) {
+        // keeps the weight reads inside the loop: hoisted, they would take
+        // 128 registers and halve the waves per SIMD
+        asm volatile("" ::: "memory");
+        if (m0 + mstep < m_end) load_q(m0 + mstep, bq2);
         block(m0, bq);
-        if (m0 + 16 >= m_end) break;
-        if (m0 + 32 < m_end) load_q(m0 + 32, bq);
-        block(m0 + 16, bq2);
+        if (m0 + mstep >= m_end) break;
+        if (m0 + 2 * mstep < m_end) load_q(m0 + 2 * mstep, bq);
+        block(m0 + mstep, bq2);
     }
     // the RoPE part, appended unchanged
-    if (blockIdx.x == 0 && a.d_rope > 0) {
+    if (tl.slice == 0 && a.d_rope > 0) {
         for (int e = threadIdx.x; e < (m_end - m_begin) * (a.d_rope / 8); e += 256) {
             const int m = m_begin + e / (a.d_rope / 8), pc = e % (a.d_rope / 8);
             *(u32x4 *)(a.q_abs + ((size_t)m * kHeads + h) * D + kLatent + 8 * pc) =
@@ -2056,43 +2081,96 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
     }
 }
 
-// grid (4 slices of 64 value dimensions, 64 heads, query chunks of
-// kAbsorbRows), 256 threads: wave w computes value dimensions i0 + 16w ..
-// i0 + 16w + 15; W_UV[h] rows are k-contiguous and go to registers directly.
-// o (fp32) enters the MFMA as bf16 hi + lo (the truncated value and the
-// rounded remainder, ~16 bits).
+// grid 4 slices of 64 value dimensions x 64 heads x query chunks (abs_tile),
+// 256 threads.  W_UV[h] rows are k-contiguous: the slice's 64 rows (64 KiB)
+// are staged in LDS (row stride 1,040 B, so the 16-byte A-operand reads of
+// eight rows at a time fall in distinct banks) and read per k-step.  o
+// (fp32) enters the MFMA as bf16 hi + lo (the truncated value and the
+// rounded remainder, ~16 bits); a block's o rows are loaded in two halves of
+// k, the first half computed while the second is in flight (two work-groups
+// per CU hide the rest).
 __global__ __launch_bounds__(256) void k_project(AbsorbArgs a) {
-    const int h = blockIdx.y, i0 = 64 * blockIdx.x;
+    constexpr int RS = kLatent * 2 + 16;
+    constexpr int KS = kLatent / 32, KH = KS / 2;
+    __shared__ __attribute__((aligned(16))) uint8_t wl[64 * RS];
+    const AbsTile tl = abs_tile(kVdim / 64, (a.n_q + kAbsorbRows - 1) / kAbsorbRows);
+    const int h = tl.head, i0 = 64 * tl.slice;
     const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
-    const int m_begin = kAbsorbRows * blockIdx.z;
+    const int m_begin = kAbsorbRows * tl.chunk;
     const int m_end = m_begin + kAbsorbRows < a.n_q ? m_begin + kAbsorbRows : a.n_q;
-    bf16x8 wa[kLatent / 32];
-    {
-        const uint16_t *W = a.w_uv + ((size_t)h * kVdim + i0 + 16 * w + n) * kLatent + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < kLatent / 32; ks++) wa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(W + 32 * ks));
-    }
-    for (int m0 = m_begin; m0 < m_end; m0 += 16) {
+    const bool by_tile = m_end - m_begin <= 48;
+    const int mb0 = by_tile ? m_begin : m_begin + 16 * w, mstep = by_tile ? 16 : 64;
+    // half hf of this lane's o row in a 16-query block: k = 32 ks + 8 g .. + 7
+    // for ks in [KH hf, KH hf + KH)
+    auto load_o = [&](int m0, int hf, f32x4 (&x)[2 * KH]) {
         const int m = m0 + n;
-        const float *op = a.o + ((size_t)(m < m_end ? m : m_begin) * kHeads + h) * kLatent + 8 * g;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float *op = a.o + ((size_t)(m < m_end ? m : m_begin) * kHeads + h) * kLatent + 8 * g + 32 * KH * hf;
 #pragma unroll
-        for (int ks = 0; ks < kLatent / 32; ks++) {
-            f32x4 x0 = *(const f32x4 *)(op + 32 * ks), x1 = *(const f32x4 *)(op + 32 * ks + 4);
-            if (m >= m_end) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 bh, bl;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float v = j < 4 ? x0[j] : x1[j - 4];
-                const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
-                bh[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
-                bl[j] = __builtin_bit_cast(__bf16, bf16_rne(v - __uint_as_float(hb)));
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], bl, acc, 0, 0, 0);
+        for (int ks = 0; ks < KH; ks++) {
+            x[2 * ks] = *(const f32x4 *)(op + 32 * ks);
+            x[2 * ks + 1] = *(const f32x4 *)(op + 32 * ks + 4);
         }
-        if (m < m_end) *(f32x4 *)(a.ctx + ((size_t)m * kHeads + h) * kVdim + i0 + 16 * w + 4 * g) = acc;
+    };
+    {
+        const uint8_t *W = reinterpret_cast<const uint8_t *>(a.w_uv + ((size_t)h * kVdim + i0) * kLatent);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int e = threadIdx.x + 256 * i, r = e >> 6, pc = e & 63;
+            *(u32x4 *)(wl + r * RS + 16 * pc) = *(const u32x4 *)(W + (size_t)r * kLatent * 2 + 16 * pc);
+        }
     }
+    __syncthreads();
+    // one tile per wave (ONE: tile w) or all four; a lane past m_end reads
+    // a valid row and stores nothing
+    auto run = [&](auto one_tile) {
+        constexpr bool ONE = decltype(one_tile)::value;
+        constexpr int NT = ONE ? 1 : 4;
+        const int tb = ONE ? w : 0;
+        for (int m0 = mb0; m0 < m_end; m0 += mstep) {
+            // keeps the weight reads inside the loop: hoisted, the 64 KiB
+            // slice would take 256 registers and leave one wave per SIMD
+            asm volatile("" ::: "memory");
+            f32x4 xa[2 * KH], xb[2 * KH];
+            load_o(m0, 0, xa);
+            load_o(m0, 1, xb);
+            f32x4 acc[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            auto half = [&](int hf, const f32x4 (&x)[2 * KH]) {
+#pragma unroll
+                for (int ks = 0; ks < KH; ks++) {
+                    bf16x8 bh, bl;
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        const float v = j < 4 ? x[2 * ks][j] : x[2 * ks + 1][j - 4];
+                        const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+                        bh[j] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+                        bl[j] = (__bf16)(v - __uint_as_float(hb));     // exact difference, rounded to nearest even
+                    }
+                    const int kk = KH * hf + ks;
+#pragma unroll
+                    for (int tt = 0; tt < NT; tt++) {
+                        const bf16x8 wa = __builtin_bit_cast(
+                            bf16x8, *(const u32x4 *)(wl + (16 * (tb + tt) + n) * RS + 64 * kk + 16 * g));
+                        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, bh, acc[tt], 0, 0, 0);
+                        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, bl, acc[tt], 0, 0, 0);
+                    }
+                }
+            };
+            half(0, xa);
+            half(1, xb);
+            const int m = m0 + n;
+            if (m < m_end) {
+#pragma unroll
+                for (int tt = 0; tt < NT; tt++)
+                    *(f32x4 *)(a.ctx + ((size_t)m * kHeads + h) * kVdim + i0 + 16 * (tb + tt) + 4 * g) = acc[tt];
+            }
+        }
+    };
+    if (by_tile)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 }
 
 // ---------------------------------------------------------------- launchers
@@ -2210,12 +2288,13 @@ hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st) {
 
 namespace dsa {
 hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_absorb, dim3(kLatent / 64, kHeads, (a.n_q + kAbsorbRows - 1) / kAbsorbRows), dim3(256), 0,
-                       st, a);
+    static_assert(kHeads == 64, "abs_tile deals 8 heads to each of 8 XCDs");
+    hipLaunchKernelGGL(k_absorb, dim3(kLatent / 64 * kHeads * ((a.n_q + kAbsorbRows - 1) / kAbsorbRows)), dim3(256),
+                       0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_project(const AbsorbArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_project, dim3(kVdim / 64, kHeads, (a.n_q + kAbsorbRows - 1) / kAbsorbRows), dim3(256), 0,
+    hipLaunchKernelGGL(k_project, dim3(kVdim / 64 * kHeads * ((a.n_q + kAbsorbRows - 1) / kAbsorbRows)), dim3(256), 0,
                        st, a);
     return hipGetLastError();
 }

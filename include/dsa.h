@@ -219,7 +219,8 @@ int dsa_pool_append(int32_t n_seq, const int32_t *n_tok, const int32_t *n_new, i
  * query that dsa_mla_attend and dsa_decode_step take.
  *   q_nope [n_q][64][256] bf16, q_rope [n_q][64][d_rope] bf16 (NULL if
  *   d_rope is 0), w_uk [64][256][512] bf16 (the model's key up-projection
- *   rows), q_abs [n_q][64][512 + d_rope] bf16.  d_rope is 0 or 64. */
+ *   rows), q_abs [n_q][64][512 + d_rope] bf16.  d_rope is 0 or 64.
+ * 1 <= n_q <= 2^20 (DSA_ERR_ARG below 1, DSA_ERR_UNSUPPORTED above). */
 int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const dsa_bf16 *q_rope,
                      const dsa_bf16 *w_uk, dsa_bf16 *q_abs, hipStream_t stream);
 
@@ -227,7 +228,8 @@ int dsa_absorb_query(int32_t n_q, int32_t d_rope, const dsa_bf16 *q_nope, const 
  * o [n_q][64][512] fp32 (the attention output), w_uv [64][256][512] bf16
  * (the model's value up-projection rows), ctx [n_q][64][256] fp32.  o
  * enters the bf16 MFMA as two halves (truncated value + rounded
- * remainder); |error| <= 2^-14 * sum_j |o_j w_ij|. */
+ * remainder); |error| <= 2^-14 * sum_j |o_j w_ij|.  1 <= n_q <= 2^20, as
+ * for dsa_absorb_query. */
 int dsa_project_output(int32_t n_q, const float *o, const dsa_bf16 *w_uv, float *ctx, hipStream_t stream);
 
 /* 7. Indexer input preparation (TensorSharp2 "The sparse-attention path":

@@ -35,7 +35,7 @@ def _host16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("n_q", [1, 8, 37])
+@pytest.mark.parametrize("n_q", [1, 8, 37, 130, 300])
 @pytest.mark.parametrize("d_rope", [64, 0])
 def test_absorb_matches_oracle(n_q, d_rope):
     """q_abs within 1 bf16 ulp of the oracle, or within the fp32 accumulation
@@ -61,7 +61,7 @@ def test_absorb_matches_oracle(n_q, d_rope):
     assert ok.all() and exact >= 0.99
 
 
-@pytest.mark.parametrize("n_q", [1, 8, 37])
+@pytest.mark.parametrize("n_q", [1, 8, 37, 130, 300])
 def test_project_matches_oracle(n_q):
     """ctx within 2^-14 sum_j |o_j W_ij| of the oracle (o as bf16 hi + lo)."""
     log(f"project n_q={n_q}")
@@ -104,3 +104,14 @@ def test_absorbed_decode_step_end_to_end():
     err = row_rel_err(ctx.cpu().numpy(), ref)
     log(f"absorbed step: ctx row-rel err {err:.3e}")
     assert err <= ATTN_TOL
+
+
+def test_absorption_query_count_bounds():
+    """n_q below 1 or above 2^20 is refused before any launch (the 1-D grid of
+    512 work-groups per 64 queries must stay under 2^32 work-items)."""
+    log("absorption n_q bounds")
+    buf = torch.zeros(1 << 16, dtype=torch.int16, device="cuda")
+    p = buf.data_ptr()
+    for n_q, want in ((0, B.DSA_ERR_ARG), ((1 << 20) + 1, B.DSA_ERR_UNSUPPORTED)):
+        assert B._lib.dsa_absorb_query(n_q, 0, p, None, p, p, None) == want
+        assert B._lib.dsa_project_output(n_q, p, p, p, None) == want
