@@ -91,7 +91,7 @@ def prefill_score_flops(w) -> int:
 
 def cpu_baseline(w, budget_s: float):
     """The oracle as it stands, on whole steps of the same workload, repeated
-    until about budget_s seconds of wall time have passed (at most 4 steps)."""
+    until about budget_s seconds of wall time have passed (at most 64 steps)."""
     from oracle import oracle as O
     threads = O.max_threads()
     done, t0 = 0, time.perf_counter()
@@ -99,7 +99,7 @@ def cpu_baseline(w, budget_s: float):
         O.decode_step(w.geom, w.q_seq, w.q_nvis, w.idx_q, w.idx_w, w.idx_k, w.q, w.cache)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 4:
+        if el >= budget_s or done >= 64:
             break
     return {"value": round(done * w.n_q / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} full step(s) of the same workload ({done * w.n_q} queries), "
@@ -152,7 +152,7 @@ def main() -> int:
                     help="query rows per sequence at the last positions (speculative verify; m128k only)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=6.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--producer", action="store_true",
                     help="time the k-pool key producer instead: one bulk append of 2^20 - 1 tokens")
     ap.add_argument("--absorb", action="store_true",
