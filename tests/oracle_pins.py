@@ -12,6 +12,8 @@ from __future__ import annotations
 
 import math
 
+import os
+
 import numpy as np
 
 from oracle import oracle as O
@@ -189,6 +191,48 @@ def pin_topk_written_rows(L):
     sel, cnt = O.topk([3], 1, 4, np.array([[9.0, -1.0, 2.0]], dtype=np.float32), L=L)
     assert sel[0, :cnt[0]].tolist() == [0, 1, 2]
     assert brute_select([9.0, -1.0, 2.0], 3, 1, 4, dense_fallback=False) == [0, 1, 2]
+
+
+def _golden(name):
+    """key -> list of int values of a tests/golden fixture (# lines are
+    comments; a line is a key followed by values, or key value pairs)."""
+    out = {}
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if not line:
+                continue
+            if len(line) == 2:
+                out[line[0]] = int(line[1])
+            else:
+                for k, v in zip(line[0::2], line[1::2]):
+                    out[k] = int(v)
+    return out
+
+
+def pin_topk_kpool_branch_from_the_pages(L):
+    """The pages' worked case (tests/golden/kpool_branch_2100.txt): over a
+    2,100-token prompt the k-pool selection is sparse exactly at positions
+    2051..2099, and at 2,052 cached tokens keeps 512 of 513 pools = 2,048
+    pooled positions (no tail).  Scores are random pool scores."""
+    g = _golden("kpool_branch_2100.txt")
+    kp, k, T = g["kpool"], g["top_k"], g["prompt_tokens"]
+    rng = np.random.default_rng(2100)
+    n_vis = np.arange(1, T + 1, dtype=np.int32)              # position p sees p + 1 tokens
+    s = rng.standard_normal((T, T // kp)).astype(np.float32)
+    sel, cnt = O.topk(n_vis, kp, k, s, L=L)
+    sparse = [p for p in range(T) if cnt[p] < n_vis[p]]
+    assert sparse == list(range(g["first_sparse_position"], g["last_sparse_position"] + 1))
+    p = g["at_cached"] - 1
+    rows = sel[p, :cnt[p]]
+    assert g["at_cached"] // kp == g["complete_pools"]
+    assert cnt[p] == g["pooled_positions"] and len(set((rows // kp).tolist())) == g["kept_pools"]
+    # every kept pool whole, and exactly the best pools by (score desc, pool asc)
+    pools = np.unique(rows // kp)
+    assert np.array_equal(np.sort(rows), np.sort((pools[:, None] * kp + np.arange(kp)).ravel()))
+    order = np.lexsort((np.arange(g["complete_pools"]), -s[p, :g["complete_pools"]]))
+    assert np.array_equal(pools, np.sort(order[:g["kept_pools"]]))
 
 
 def pin_topk_invariants(L):
