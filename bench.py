@@ -227,12 +227,14 @@ def main() -> int:
         B.set_timing_events(evs[i])
         reps[i % R].decode_step()
     B.set_timing_events(None)
+    ran = B.timing_ran()                # the same kernels run at every step of one workload
     torch.cuda.synchronize()
     names = KERNELS
     per = {k: 0.0 for k in names}
     for row in evs:
         for j, k in enumerate(names):
-            per[k] += row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3 / n_rep
+            if (ran >> j) & 1:          # a kernel that did not run leaves its events unrecorded
+                per[k] += row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3 / n_rep
     score_us = per["score"]
     prefill = w.n_seq == 1 and w.n_q > 1
     if prefill:

@@ -29,7 +29,8 @@ class Batch(ctypes.Structure):
 
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
            "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_index_prepare",
-           "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events", "dsa_stream_read")
+           "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events", "dsa_timing_ran",
+           "dsa_stream_read")
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -53,6 +54,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_device_check": (ctypes.c_int, []),
         "dsa_set_timing_events": (ctypes.c_int, [P, i32]),
+        "dsa_timing_ran": (i32, []),
         "dsa_stream_read": (ctypes.c_int, [P, sz, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -226,6 +228,12 @@ def stream_read(buf, sink, stream=None) -> None:
         raise TypeError("buf: a contiguous cuda tensor; sink: an int32 cuda tensor")
     _check(_lib.dsa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
            "dsa_stream_read")
+
+
+def timing_ran() -> int:
+    """Bit i set: the last dsa_decode_step on this thread ran kernel i
+    (score, filter, select, attend, merge)."""
+    return int(_lib.dsa_timing_ran())
 
 
 def set_timing_events(events) -> None:

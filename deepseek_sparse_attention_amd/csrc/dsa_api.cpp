@@ -36,6 +36,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t *g_events = nullptr;
 thread_local int32_t g_n_events = 0;
+thread_local int32_t g_ran = 0;   // kernels the last dsa_decode_step on this thread ran (bit i: kernel i)
 
 // Queries per absorption call: keeps the 1-D grid (512 work-groups of 256
 // threads per 64 queries) under 2^32 work-items.
@@ -189,6 +190,8 @@ const char *dsa_status_str(int s) {
 }
 
 const char *dsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dsa_timing_ran(void) { return g_ran; }
 
 int dsa_set_timing_events(hipEvent_t *events, int32_t n_events) {
     g_events = (events && n_events > 0) ? events : nullptr;
@@ -353,15 +356,12 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
         a.fused = 1;
         hipEvent_t ev[10];
         for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
+        g_ran = 0;
         DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream, ev[0], ev[1]), "score"));
-        if (!a.select_scan) {
-            DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
-        } else {
-            for (int i = 2; i < 4; i++)
-                if (ev[i]) (void)hipEventRecord(ev[i], stream);
-        }
+        if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
         DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
         DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
+        g_ran = 1 | (a.select_scan ? 0 : 2) | 4 | 8 | (a.n_split > 1 ? 16 : 0);
         return (int)DSA_OK;
     });
 }

@@ -2244,7 +2244,7 @@ hipError_t launch_select(const Args &a, hipStream_t st, hipEvent_t ev0, hipEvent
 }
 
 // The attention kernel takes ev[0] and ev[1], the split merge ev[2] and
-// ev[3] (recorded back to back when there is no merge); ev may be NULL.
+// ev[3] (not recorded when there is no merge); ev may be NULL.
 hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev) {
     const hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     if (a.attn_hs == 2) {
@@ -2266,11 +2266,7 @@ hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.n_split == 1) {
-        if (ev && ev[2]) (void)hipEventRecord(ev[2], st);
-        if (ev && ev[3]) (void)hipEventRecord(ev[3], st);
-        return e;
-    }
+    if (a.n_split == 1) return e;
     DSA_LAUNCH(ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, k_reduce, dim3(kHeads, a.n_q), dim3(128), st, a);
     return hipGetLastError();
 }

@@ -269,11 +269,16 @@ int dsa_index_prepare(const dsa_geometry *geom, const dsa_batch *batch, double r
  * (hipExtLaunchKernel: the marks come from the dispatch, so
  * elapsed(events[2 i], events[2 i + 1]) is the kernel's execution time, as a
  * kernel trace reports it), as many as fit.  Kernel order: score, filter,
- * select, attend, split merge (ten events in all); a kernel the call does
+ * select, attend, split merge (ten events in all).  A kernel the call does
  * not run (the filter of a one-kernel top-k, the merge of an unsplit
- * attention) has its two events recorded back to back.  Pass NULL/0 to
- * stop.  Returns DSA_OK. */
+ * attention) leaves its two events unrecorded; dsa_timing_ran tells which
+ * ran.  Pass NULL/0 to stop.  Returns DSA_OK. */
 int dsa_set_timing_events(hipEvent_t *events, int32_t n_events);
+
+/* Bit i set: the last successful dsa_decode_step on this thread ran kernel i
+ * of the order above (score 1, filter 2, select 4, attend 8, merge 16).
+ * Host only; 0 before the first such call. */
+int32_t dsa_timing_ran(void);
 
 /* Bandwidth probe for benchmarks: reads bytes (a multiple of 16) from the
  * 16-byte aligned device buffer buf with non-temporal 16-byte loads in a

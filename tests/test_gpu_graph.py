@@ -81,3 +81,48 @@ def test_stream_read_probe():
         B.stream_read(buf[:100], sink)
     with pytest.raises(B.DSAError):
         B.stream_read(buf[1:1 + 4096], sink)
+
+
+# name, geometry, n_seq, T, q_seq, q_nvis, whether the filter kernel runs
+# (rows > 16,384), whether the merge runs (more than one split)
+TIMED = [
+    ("tok_chunked", dict(I.GEOM_TOKEN), 4, 40000, [0, 1, 2, 3, 0], [40000, 30001, 20480, 1500, 0], True, True),
+    ("one_query_scan", dict(I.GEOM_TOKEN), 1, 9000, [0], [9000], False, True),
+]
+
+
+@pytest.mark.parametrize("case", TIMED, ids=[c[0] for c in TIMED])
+def test_timing_events_time_the_kernels_that_ran(case):
+    """With timing events set, the step gives the same outputs, reports the
+    kernels it ran (the filter only for the chunked top-k), and each of them
+    has a positive start-to-stop interval inside the call's own bracket."""
+    name, g, n_seq, T, q_seq, q_nvis, filt, merge = case
+    log(f"timing events {name}")
+    w = I.make_workload(name, 301, g, n_seq, T, q_seq, q_nvis)
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dw.sel, dw.sel_count, dw.out, dw.lse)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    evs[10].record()
+    B.set_timing_events(evs[:10])
+    try:
+        dw.decode_step()
+    finally:
+        B.set_timing_events(None)
+    evs[11].record()
+    torch.cuda.synchronize()
+    ran = B.timing_ran()
+    assert ran & 0b01101 == 0b01101, f"score, select and attend always run: {ran:#b}"
+    assert bool(ran & 0b00010) == filt and bool(ran & 0b10000) == merge, f"{ran:#b}"
+    whole = evs[10].elapsed_time(evs[11])
+    for j in range(5):
+        if (ran >> j) & 1:
+            t0, t1 = evs[10].elapsed_time(evs[2 * j]), evs[10].elapsed_time(evs[2 * j + 1])
+            assert 0.0 <= t0 < t1 <= whole, f"kernel {j}: [{t0}, {t1}] outside [0, {whole}] ms"
+    for got, want in zip((dw.sel, dw.sel_count, dw.out.nan_to_num(7.0), dw.lse.nan_to_num(7.0)),
+                         (ref[0], ref[1], ref[2].nan_to_num(7.0), ref[3].nan_to_num(7.0))):
+        assert torch.equal(got, want)
