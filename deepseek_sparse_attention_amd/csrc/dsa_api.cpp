@@ -38,6 +38,10 @@ thread_local hipEvent_t *g_events = nullptr;
 thread_local int32_t g_n_events = 0;
 thread_local int32_t g_ran = 0;   // kernels the last dsa_decode_step on this thread ran (bit i: kernel i)
 
+// Queries per call of the attention path: its kernels take one grid row
+// (gridDim.y) per query.
+constexpr int32_t kMaxQueries = 65535;
+
 // Queries per absorption call: keeps the 1-D grid (512 work-groups of 256
 // threads per 64 queries) under 2^32 work-items.
 constexpr int32_t kMaxAbsorbQueries = 1 << 20;
@@ -92,6 +96,7 @@ int check_geometry(const dsa_geometry *g) {
 int check_batch(const dsa_batch *b) {
     if (!b) return fail(DSA_ERR_ARG, "batch is NULL");
     if (b->n_q < 1) return fail(DSA_ERR_ARG, "n_q must be >= 1");
+    if (b->n_q > kMaxQueries) return fail(DSA_ERR_UNSUPPORTED, "n_q must be <= 65535 (one grid row per query)");
     if (b->n_seq < 1) return fail(DSA_ERR_ARG, "n_seq must be >= 1");
     if (!b->q_nvis) return fail(DSA_ERR_ARG, "q_nvis is NULL");
     if (!b->q_seq && b->n_q > b->n_seq) return fail(DSA_ERR_ARG, "q_seq NULL needs n_q <= n_seq");
@@ -213,7 +218,8 @@ int dsa_device_check(void) {
 }
 
 size_t dsa_workspace_bytes(const dsa_geometry *g, int32_t n_q, int64_t max_nvis) {
-    if (check_geometry(g) != DSA_OK || n_q < 1 || max_nvis < 1 || max_nvis > (int64_t)INT32_MAX) return 0;
+    if (check_geometry(g) != DSA_OK || n_q < 1 || n_q > kMaxQueries || max_nvis < 1 || max_nvis > (int64_t)INT32_MAX)
+        return 0;
     return dsa::make_plan(g->kpool, g->top_k, g->d_rope, n_q, max_nvis).total;
 }
 

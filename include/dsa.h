@@ -102,7 +102,8 @@ typedef struct {
  * positions p of one sequence with n_vis = p + 1 (a query sees its own
  * token).  "rows(q)" below is q_nvis[q] / kpool. */
 typedef struct {
-    int32_t n_q;                 /* number of queries (>= 1)                          */
+    int32_t n_q;                 /* number of queries, 1..65535 (DSA_ERR_UNSUPPORTED
+                                    above)                                            */
     int32_t n_seq;               /* number of sequences in the cache arrays (>= 1)    */
     const int32_t *q_seq;        /* device [n_q] sequence of each query; NULL: query i
                                     reads sequence i (then n_q <= n_seq)              */
@@ -116,7 +117,7 @@ typedef struct {
 /* Bytes of workspace that dsa_topk, dsa_mla_attend and dsa_decode_step need
  * for this geometry, query count and visible bound (the maximum of the three;
  * one workspace serves all of them).  Returns 0 for an unsupported geometry
- * or non-positive sizes. */
+ * or sizes out of range (n_q outside 1..65535, max_nvis outside 1..2^31 - 1). */
 size_t dsa_workspace_bytes(const dsa_geometry *geom, int32_t n_q, int64_t max_nvis);
 
 /* Zero-fills ws_bytes of a workspace on the stream (a fill kernel, no
