@@ -109,3 +109,84 @@ def test_good_call_after_rejected_ones(dw):
     sel, cnt = O.topk(w.q_nvis, 1, w.geom["top_k"], scores)
     assert np.array_equal(dw.sel_count.cpu().numpy(), cnt)
     assert np.array_equal(dw.sel.cpu().numpy(), sel)
+
+
+def _entry_calls(dw, scores, score_ld):
+    """(name, thunk) for each entry point of the path on dw's tensors."""
+    g, b = dw.geom, dw.batch
+    return [
+        ("dsa_index_scores", lambda: B.index_scores(g, b, dw.idx_q, dw.idx_w, dw.idx_k, dw.w.key_rows, scores,
+                                                     score_ld)),
+        ("dsa_topk", lambda: B.topk(g, b, scores, score_ld, dw.sel, dw.sel_ld, dw.sel_count, dw.ws)),
+        ("dsa_mla_attend", lambda: B.mla_attend(g, b, dw.q, dw.cache, dw.w.T, dw.sel, dw.sel_ld, dw.sel_count,
+                                                 dw.out, dw.lse, dw.ws)),
+        ("dsa_decode_step", lambda: dw.decode_step()),
+        ("dsa_workspace_init", lambda: B._check(B._lib.dsa_workspace_init(B._ptr(dw.ws), dw.ws.numel(),
+                                                                          B._stream(None)), "init")),
+    ]
+
+
+def test_injected_launch_failure_is_reported(dw, monkeypatch):
+    """DSA_TEST_FAIL_LAUNCH=1 makes every entry point take its launch-failure
+    path after its argument checks: DSA_ERR_LAUNCH with a message, nothing
+    written.  Unset, the same calls run and the step matches the oracle."""
+    log("injected launch failures")
+    score_ld = dw.max_nvis
+    scores = torch.full((dw.n_q, score_ld), 5.0, device="cuda")
+    torch.cuda.synchronize()
+    dw.sel.fill_(-7)
+    monkeypatch.setenv("DSA_TEST_FAIL_LAUNCH", "1")
+    for name, call in _entry_calls(dw, scores, score_ld):
+        with pytest.raises(B.DSAError) as e:
+            call()
+        assert e.value.status == B.DSA_ERR_LAUNCH, f"{name}: {e.value}"
+        assert "injected" in str(e.value), f"{name}: {e.value}"
+    torch.cuda.synchronize()
+    assert bool((scores == 5.0).all()) and bool((dw.sel == -7).all()), "a failed launch wrote its outputs"
+    monkeypatch.delenv("DSA_TEST_FAIL_LAUNCH")
+    for name, call in _entry_calls(dw, scores, score_ld):
+        call()
+    torch.cuda.synchronize()
+    test_good_call_after_rejected_ones(dw)
+
+
+def test_split_entry_points_check_their_own_arguments(dw):
+    """dsa_index_scores, dsa_topk and dsa_mla_attend refuse short row
+    strides, NULL outputs and a short workspace with their documented
+    statuses."""
+    log("split entry point checks")
+    g, b = B.geometry(dw.geom), dw.batch
+    score_ld = dw.max_nvis
+    scores = torch.zeros((dw.n_q, score_ld), device="cuda")
+    P, s = B._ptr, B._stream(None)
+    ws, n_ws = P(dw.ws), dw.ws.numel()
+    L = B._lib
+    cases = [
+        ("scores: key stride", L.dsa_index_scores(ctypes.byref(g), ctypes.byref(b), P(dw.idx_q), P(dw.idx_w),
+                                                  P(dw.idx_k), dw.max_nvis - 1, P(scores), score_ld, s),
+         B.DSA_ERR_ARG),
+        ("scores: score_ld", L.dsa_index_scores(ctypes.byref(g), ctypes.byref(b), P(dw.idx_q), P(dw.idx_w),
+                                                P(dw.idx_k), dw.w.key_rows, P(scores), dw.max_nvis - 1, s),
+         B.DSA_ERR_ARG),
+        ("scores: NULL scores", L.dsa_index_scores(ctypes.byref(g), ctypes.byref(b), P(dw.idx_q), P(dw.idx_w),
+                                                   P(dw.idx_k), dw.w.key_rows, None, score_ld, s), B.DSA_ERR_ARG),
+        ("topk: score_ld", L.dsa_topk(ctypes.byref(g), ctypes.byref(b), P(scores), dw.max_nvis - 1, P(dw.sel),
+                                      dw.sel_ld, P(dw.sel_count), ws, n_ws, s), B.DSA_ERR_ARG),
+        ("topk: sel_ld", L.dsa_topk(ctypes.byref(g), ctypes.byref(b), P(scores), score_ld, P(dw.sel),
+                                    dw.sel_ld - 1, P(dw.sel_count), ws, n_ws, s), B.DSA_ERR_ARG),
+        ("topk: NULL count", L.dsa_topk(ctypes.byref(g), ctypes.byref(b), P(scores), score_ld, P(dw.sel),
+                                        dw.sel_ld, None, ws, n_ws, s), B.DSA_ERR_ARG),
+        ("topk: short workspace", L.dsa_topk(ctypes.byref(g), ctypes.byref(b), P(scores), score_ld, P(dw.sel),
+                                             dw.sel_ld, P(dw.sel_count), ws, 256, s), B.DSA_ERR_WORKSPACE),
+        ("attend: cache stride", L.dsa_mla_attend(ctypes.byref(g), ctypes.byref(b), P(dw.q), P(dw.cache),
+                                                  dw.max_nvis - 1, P(dw.sel), dw.sel_ld, P(dw.sel_count),
+                                                  P(dw.out), P(dw.lse), ws, n_ws, s), B.DSA_ERR_ARG),
+        ("attend: NULL sel", L.dsa_mla_attend(ctypes.byref(g), ctypes.byref(b), P(dw.q), P(dw.cache), dw.w.T,
+                                              None, dw.sel_ld, P(dw.sel_count), P(dw.out), P(dw.lse), ws, n_ws, s),
+         B.DSA_ERR_ARG),
+        ("attend: no workspace", L.dsa_mla_attend(ctypes.byref(g), ctypes.byref(b), P(dw.q), P(dw.cache), dw.w.T,
+                                                  P(dw.sel), dw.sel_ld, P(dw.sel_count), P(dw.out), P(dw.lse), None,
+                                                  0, s), B.DSA_ERR_WORKSPACE),
+    ]
+    for name, got, want in cases:
+        assert got == want, f"{name}: status {got}, want {want} ({B._lib.dsa_last_error().decode()})"
