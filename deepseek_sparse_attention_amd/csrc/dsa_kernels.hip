@@ -254,18 +254,46 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(16))) uint8_t tiles[4][64 * 256];
     const int q = blockIdx.y;
+    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+    u32x4 v[16];
+    // With q_seq NULL (query q reads sequence q < n_seq) and one tile per
+    // work-group, the wave's first step of keys is requested before the
+    // query's fields return.  Rows are clamped below the batch's row bound
+    // max_nvis / kpool (<= key_stride): every such row lies in the caller's
+    // [n_seq][key_stride] buffer, and rows at or past the query's own are
+    // neither scored nor counted.
+    const int64_t rmax = a.max_nvis / a.kpool;
+    const bool early = !STRIDE && a.q_seq == nullptr && rmax >= 1;
+    if (early) {
+        const uint8_t *K0 = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)q * a.key_stride * kIdxDim);
+        const int64_t b0 = (int64_t)blockIdx.x * a.score_tile + 64 * w;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            int64_t r = b0 + 4 * i + (lane >> 4);
+            r = r < rmax ? r : rmax - 1;
+            v[i] = __builtin_nontemporal_load((const u32x4 *)(K0 + r * 256 + 16 * (lane & 15)));
+        }
+    }
+    // a wave leaving without using them waits for its early loads first
+    auto drain = [&] {
+        if (early) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
     const QInfo qi = query_info(a, q);
-    if (qi.mode == 2) return;
-    if (a.fused && qi.mode == 0) return;
-    if (a.prefill && qi.seq == query_seq(a, pf_leader(a, q))) return;   // done by k_score_prefill
+    if (qi.mode == 2 || (a.fused && qi.mode == 0) ||
+        (a.prefill && qi.seq == query_seq(a, pf_leader(a, q)))) {   // the last: done by k_score_prefill
+        drain();
+        return;
+    }
     const int64_t rows = qi.rows;
-    if ((int64_t)blockIdx.x * a.score_tile >= rows) return;
+    if ((int64_t)blockIdx.x * a.score_tile >= rows) {
+        drain();
+        return;
+    }
     const bool hist = a.fused != 0;
     if (hist) {
         for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
         __syncthreads();
     }
-    const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
 
     bf16x8 qa[2][4];
     float wt[2][4];
@@ -274,8 +302,8 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     for (int mb = 0; mb < 2; mb++) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            u32x4 v = *(const u32x4 *)(qip + (16 * mb + n) * kIdxDim + 32 * s + 8 * g);
-            qa[mb][s] = __builtin_bit_cast(bf16x8, v);
+            const u32x4 t = *(const u32x4 *)(qip + (16 * mb + n) * kIdxDim + 32 * s + 8 * g);
+            qa[mb][s] = __builtin_bit_cast(bf16x8, t);
         }
 #pragma unroll
         for (int r = 0; r < 4; r++) wt[mb][r] = a.idx_w[(size_t)q * kIdxHeads + 16 * mb + 4 * g + r];
@@ -284,7 +312,6 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     float *srow = a.scores + (size_t)q * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
     uint8_t *tb = tiles[w];
-    u32x4 v[16];
     auto fetch = [&](int64_t base) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -299,7 +326,11 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
          t0 = STRIDE ? t0 + (int64_t)gridDim.x * a.score_tile : rows) {
     const int64_t end = t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
     int64_t base = t0 + 64 * w;
-    if (base < end) fetch(base);
+    if (early) {
+        if (base >= end) drain();              // no step for this wave in a short last tile
+    } else if (base < end) {
+        fetch(base);
+    }
     for (; base < end; base += 256) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {

@@ -24,7 +24,11 @@ def run_hint(q_seq) -> int:
 class DeviceWorkload:
     """Uploads a host ``Workload`` and owns outputs and a workspace for it."""
 
-    def __init__(self, w: Workload, device: str = "cuda", sel_ld: int | None = None):
+    def __init__(self, w: Workload, device: str = "cuda", sel_ld: int | None = None, seq_map: str = "auto"):
+        """seq_map "auto": when query i reads sequence i, the batch passes a
+        NULL q_seq (the C ABI's convention for that case, which lets the
+        scorer request its first keys before the query's fields arrive);
+        "always": the device array in every case."""
         self.w = w
         self.geom = w.geom
         dev = torch.device(device)
@@ -48,7 +52,9 @@ class DeviceWorkload:
                                device=dev)
         self.lse = torch.empty((self.n_q, self.geom["n_heads"]), dtype=torch.float32, device=dev)
         self.ws = B.new_workspace(self.geom, self.n_q, self.max_nvis, device=dev)
-        self.batch = B.batch(self.q_seq, self.q_nvis, self.max_nvis, w.n_seq, run_hint(w.q_seq))
+        identity = w.n_q <= w.n_seq and np.array_equal(w.q_seq, np.arange(w.n_q))
+        self.batch = B.batch(None if (identity and seq_map == "auto") else self.q_seq, self.q_nvis, self.max_nvis,
+                             w.n_seq, run_hint(w.q_seq))
 
     def decode_step(self, stream=None, with_sel: bool = True) -> None:
         B.decode_step(self.geom, self.batch, self.idx_q, self.idx_w, self.idx_k, self.w.key_rows, self.q,

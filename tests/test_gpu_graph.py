@@ -126,3 +126,29 @@ def test_timing_events_time_the_kernels_that_ran(case):
     for got, want in zip((dw.sel, dw.sel_count, dw.out.nan_to_num(7.0), dw.lse.nan_to_num(7.0)),
                          (ref[0], ref[1], ref[2].nan_to_num(7.0), ref[3].nan_to_num(7.0))):
         assert torch.equal(got, want)
+
+
+# identity sequence maps with dense, invalid and short-tile queries: the
+# scorer's early first fetch (NULL map) against the explicit map
+NULL_MAP = [
+    ("tok", dict(I.GEOM_TOKEN), 4, 40000, [0, 1, 2, 3], [40000, 1500, 0, 17001]),
+    ("pool", dict(I.GEOM_TOKEN, kpool=4, d_rope=0), 3, 90001, [0, 1, 2], [90001, 2051, 8195]),
+]
+
+
+@pytest.mark.parametrize("case", NULL_MAP, ids=[c[0] for c in NULL_MAP])
+def test_null_sequence_map_matches_explicit_map(case):
+    """A batch whose query i reads sequence i gives bit-identical results
+    with q_seq NULL and with the explicit map."""
+    name, g, n_seq, T, q_seq, q_nvis = case
+    log(f"NULL sequence map {name}")
+    w = I.make_workload(name, 303, g, n_seq, T, q_seq, q_nvis)
+    a, b = DeviceWorkload(w, seq_map="auto"), DeviceWorkload(w, seq_map="always")
+    assert a.batch.q_seq is None and b.batch.q_seq is not None
+    for _ in range(2):
+        a.decode_step()
+        b.decode_step()
+    torch.cuda.synchronize()
+    assert torch.equal(a.sel, b.sel) and torch.equal(a.sel_count, b.sel_count)
+    assert torch.equal(a.out.nan_to_num(7.0), b.out.nan_to_num(7.0))
+    assert torch.equal(a.lse.nan_to_num(7.0), b.lse.nan_to_num(7.0))
