@@ -5,6 +5,7 @@ library allocates nothing and records no memset, so its launches are
 capturable as they stand."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -12,6 +13,7 @@ from gpu_common import log, gpu_arch
 
 pytestmark = pytest.mark.gpu
 
+from oracle import oracle as O                                     # noqa: E402
 from deepseek_sparse_attention_amd import binding as B            # noqa: E402
 from deepseek_sparse_attention_amd import inputs as I             # noqa: E402
 from deepseek_sparse_attention_amd.workload import DeviceWorkload  # noqa: E402
@@ -133,6 +135,9 @@ def test_timing_events_time_the_kernels_that_ran(case):
 NULL_MAP = [
     ("tok", dict(I.GEOM_TOKEN), 4, 40000, [0, 1, 2, 3], [40000, 1500, 0, 17001]),
     ("pool", dict(I.GEOM_TOKEN, kpool=4, d_rope=0), 3, 90001, [0, 1, 2], [90001, 2051, 8195]),
+    ("pool_no_rows", dict(I.GEOM_TOKEN, kpool=4, d_rope=0), 2, 4, [0, 1], [3, 1]),
+    ("tok_one_row", dict(I.GEOM_TOKEN), 2, 1, [0, 1], [1, 1]),
+    ("tok_one_tile", dict(I.GEOM_TOKEN), 3, 3000, [0, 1, 2], [3000, 2049, 1023]),
 ]
 
 
@@ -152,3 +157,7 @@ def test_null_sequence_map_matches_explicit_map(case):
     assert torch.equal(a.sel, b.sel) and torch.equal(a.sel_count, b.sel_count)
     assert torch.equal(a.out.nan_to_num(7.0), b.out.nan_to_num(7.0))
     assert torch.equal(a.lse.nan_to_num(7.0), b.lse.nan_to_num(7.0))
+    kp = g["kpool"]
+    scores = O.index_scores(w.q_seq, w.q_nvis, kp, w.idx_q, w.idx_w, w.idx_k)
+    sel, cnt = O.topk(w.q_nvis, kp, g["top_k"], scores)
+    assert np.array_equal(a.sel_count.cpu().numpy(), cnt) and np.array_equal(a.sel.cpu().numpy(), sel)
