@@ -164,8 +164,8 @@ def main() -> int:
                     help="also run a plain 256 MiB device copy (to scale byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the multi-GPU sharding is a design note, not an implementation)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(sharding over several GPUs is described, not implemented)", file=sys.stderr)
         return 2
 
     if args.producer:
