@@ -129,7 +129,9 @@ int dsa_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  * for r < rows(q); other entries of the row are not written.
  *   idx_q  [n_q][n_idx_heads][d_idx] 16-bit    idx_w [n_q][n_idx_heads] fp32
  *   idx_k  [n_seq][key_seq_stride][d_idx] 16-bit (tokens, or pool keys for
- *          kpool 4; key_seq_stride >= max_nvis / kpool)
+ *          kpool 4; key_seq_stride >= max_nvis / kpool).  Any row below
+ *          max_nvis / kpool of a query's sequence may be read, whatever the
+ *          query's own length; only rows below rows(q) affect the result.
  *   scores [n_q][score_ld] fp32, score_ld >= max_nvis / kpool.
  * idx_q and idx_k are bf16, or IEEE f16 when geom->idx_f16 (the same holds
  * for dsa_decode_step).  Accumulation is fp32 over exact products; with
