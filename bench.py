@@ -91,8 +91,12 @@ def prefill_score_flops(w) -> int:
 
 def cpu_baseline(w, budget_s: float):
     """The oracle as it stands, on whole steps of the same workload, repeated
-    until about budget_s seconds of wall time have passed (at most 64 steps)."""
+    until about budget_s seconds of wall time have passed (at most 64 steps),
+    on every host thread; then on one thread, one whole step of the tiny
+    decode (one query over 4,096 tokens) and one query of the 8 x 64K decode
+    (its first sequence and query, drawn from the same seeds)."""
     from oracle import oracle as O
+    from deepseek_sparse_attention_amd import inputs as I
     threads = O.max_threads()
     done, t0 = 0, time.perf_counter()
     while True:
@@ -101,9 +105,22 @@ def cpu_baseline(w, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 64:
             break
-    return {"value": round(done * w.n_q / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} full step(s) of the same workload ({done * w.n_q} queries), "
-                      f"{el:.1f} s wall on {threads} OpenMP threads of {cpu_model()}"}
+    res = {"value": round(done * w.n_q / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} full step(s) of the same workload ({done * w.n_q} queries), "
+                     f"{el:.1f} s wall on {threads} OpenMP threads of {cpu_model()}"}
+    one = {}
+    O.set_threads(1)
+    try:
+        for name, sw in (("c0", I.config("c0")),
+                         ("c1_one_query", I.make_workload("c1", 1, I.GEOM_TOKEN, 1, 65536, [0], [65536]))):
+            t0 = time.perf_counter()
+            O.decode_step(sw.geom, sw.q_seq, sw.q_nvis, sw.idx_q, sw.idx_w, sw.idx_k, sw.q, sw.cache)
+            el = time.perf_counter() - t0
+            one[name] = {"queries_per_s": round(sw.n_q / el, 3), "s": round(el, 3)}
+    finally:
+        O.set_threads(threads)
+    res["single_thread"] = one
+    return res
 
 
 def stream_read_rate(gib: int = 1, reps: int = 20) -> dict:
@@ -211,7 +228,7 @@ def main() -> int:
     ms_step = start.elapsed_time(end) / args.steps
     qps = w.n_q / (ms_step * 1e-3)
     step_bytes, score_bytes = algorithmic_bytes(w)
-    print(f"[bench] {ms_step * 1e3:.1f} us/step, wall {wall * 1e3 / args.steps:.1f} us/step", file=sys.stderr,
+    print(f"[bench] {ms_step * 1e3:.1f} us/step, wall {wall * 1e6 / args.steps:.1f} us/step", file=sys.stderr,
           flush=True)
 
     # ---- per-kernel durations: each kernel of the same fused step launched

@@ -159,12 +159,14 @@ int launched(hipError_t e, const char *what) {
     return DSA_OK;
 }
 
-int check_ws(const dsa::Plan &p, const void *ws, size_t ws_bytes) {
+// Lays the plan out in the caller's workspace (the histogram region's size
+// follows from ws_bytes alone); refuses a workspace it does not fit.
+int check_ws(dsa::Plan &p, const void *ws, size_t ws_bytes) {
     if (!ws) return fail(DSA_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned16(ws)) return fail(DSA_ERR_ARG, "workspace must be 16-byte aligned");
-    if (ws_bytes < p.total)
+    if (!dsa::place_workspace(p, ws_bytes))
         return fail(DSA_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
-                                           std::to_string(p.total));
+                                           std::to_string(dsa::workspace_bytes(p)));
     return DSA_OK;
 }
 
@@ -220,7 +222,7 @@ int dsa_device_check(void) {
 size_t dsa_workspace_bytes(const dsa_geometry *g, int32_t n_q, int64_t max_nvis) {
     if (check_geometry(g) != DSA_OK || n_q < 1 || n_q > kMaxQueries || max_nvis < 1 || max_nvis > (int64_t)INT32_MAX)
         return 0;
-    return dsa::make_plan(g->kpool, g->top_k, g->d_rope, n_q, max_nvis).total;
+    return dsa::workspace_bytes(dsa::make_plan(g->kpool, g->top_k, g->d_rope, n_q, max_nvis));
 }
 
 int dsa_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -242,7 +244,7 @@ int dsa_index_scores(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *
         if (!idx_q || !idx_w || !idx_k || !scores) return fail(DSA_ERR_ARG, "NULL tensor pointer");
         if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(idx_k) || !aligned16(scores))
             return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
-        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
         if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
         if (score_ld < p.max_rows) return fail(DSA_ERR_ARG, "score_ld < max_nvis / kpool");
         if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
@@ -267,7 +269,7 @@ int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int
         if (!scores || !sel || !sel_count) return fail(DSA_ERR_ARG, "NULL tensor pointer");
         if (!aligned16(scores) || !aligned16(sel) || !aligned16(sel_count))
             return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
-        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
         if (score_ld < p.max_rows) return fail(DSA_ERR_ARG, "score_ld < max_nvis / kpool");
         if (sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
         DSA_TRY(check_ws(p, ws, ws_bytes));
@@ -296,7 +298,7 @@ int dsa_mla_attend(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *q,
         if (!aligned16(q) || !aligned16(cache) || !aligned16(sel) || !aligned16(sel_count) || !aligned16(out) ||
             (lse && !aligned16(lse)))
             return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
-        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
         if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
         if (sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
         DSA_TRY(check_ws(p, ws, ws_bytes));
@@ -329,7 +331,7 @@ int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *i
             (sel_count && !aligned16(sel_count)))
             return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
         if ((sel == nullptr) != (sel_count == nullptr)) return fail(DSA_ERR_ARG, "sel and sel_count go together");
-        const dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+        dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
         if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
         if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
         if (sel && sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");

@@ -1114,15 +1114,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // 16 bytes per lane from src (per-lane address) to LDS at lds + 16 * lane.
 // Issued from asm so that the compiler's wait insertion, which knows
 // nothing of it, adds no vmcnt wait in front of the LDS reads of the other
-// buffers; the kernel waits for it itself.
+// buffers; the kernel waits for it itself.  The asm sets m0 (the LDS
+// destination) and says so in its clobber list, so that no value the
+// compiler might keep in m0 is assumed to survive it; clang warns that m0 is
+// a reserved register, which is the point here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
 // The same with a uniform base address in SGPRs and a per-lane 32-bit offset.
 __device__ __forceinline__ void dma16s(const void *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {

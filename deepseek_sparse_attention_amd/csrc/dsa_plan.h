@@ -37,11 +37,25 @@ struct Plan {
     int32_t select_scan;          // 1: top-k in one kernel that scans the scores
     int32_t score_tile;           // key rows per score work-group
 
-    // workspace byte offsets; [0, ctrl_bytes) must be zero between calls
-    size_t off_hist, ctrl_bytes;
+    // workspace byte offsets (absolute once place_workspace has run): the
+    // histograms lead, the rest (the body) follows the histogram region
+    size_t off_hist;
     size_t off_thr, off_chunk, off_cand, off_scores, off_sel, off_cnt;
-    size_t off_pacc, off_pml, total;
+    size_t off_pacc, off_pml;
+    size_t body;                  // bytes after the histogram region
+    size_t hist_region;           // bytes of the histogram region (0 until placed)
 };
+
+constexpr size_t kHistQueryBytes = (size_t)kHistBins * 4;   // one query's first-digit histogram
+
+// The histogram region of a workspace of ws_bytes: its first sixteenth,
+// rounded down to whole 16 KiB histograms.  It depends on the workspace
+// size only, never on the call's shape, so calls of different query counts
+// and context lengths on one workspace all find their histograms inside
+// the same region -- which only histogram accumulation (and the clearing
+// after it) ever touches, so it is all zero between calls -- and put
+// everything else after it.
+inline size_t hist_region_bytes(size_t ws_bytes) { return (ws_bytes / 16) / kHistQueryBytes * kHistQueryBytes; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -120,8 +134,7 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.score_tile = (int32_t)tile;
 
     size_t o = 0;
-    p.off_hist = o;   o += align256((size_t)n_q * kHistBins * 4);
-    p.ctrl_bytes = o;
+    p.off_hist = 0;
     p.off_thr = o;    o += align256((size_t)n_q * 8);
     p.off_chunk = o;  o += align256((size_t)n_q * p.n_chunks * 4);
     p.off_cand = o;   o += align256((size_t)n_q * p.n_chunks * p.cand_cap * 8);
@@ -130,8 +143,34 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.off_cnt = o;    o += align256((size_t)n_q * 4);
     p.off_pacc = o;   o += align256((size_t)n_q * p.n_split * kHeads * kLatent * 4);
     p.off_pml = o;    o += align256((size_t)n_q * p.n_split * kHeads * 2 * 4);
-    p.total = o;
+    p.body = o;
+    p.hist_region = 0;
     return p;
+}
+
+// Smallest workspace for the plan: the histogram region must hold n_q
+// histograms (ws / 16 >= n_q * 16 KiB) and the body must fit after it
+// (ws - ws / 16 >= body).
+inline size_t workspace_bytes(const Plan &p) {
+    const size_t h = (size_t)p.n_q * kHistQueryBytes * 16;
+    const size_t b = (p.body * 16 + 14) / 15;
+    return align256(h > b ? h : b);
+}
+
+// Lays the plan out in a workspace of ws_bytes; false if it does not fit.
+inline bool place_workspace(Plan &p, size_t ws_bytes) {
+    const size_t h = hist_region_bytes(ws_bytes);
+    if ((size_t)p.n_q * kHistQueryBytes > h || h + p.body > ws_bytes) return false;
+    p.hist_region = h;
+    p.off_thr += h;
+    p.off_chunk += h;
+    p.off_cand += h;
+    p.off_scores += h;
+    p.off_sel += h;
+    p.off_cnt += h;
+    p.off_pacc += h;
+    p.off_pml += h;
+    return true;
 }
 
 }  // namespace dsa

@@ -29,12 +29,20 @@
  *    (size from dsa_workspace_bytes).  The library keeps no pointer after the
  *    work it enqueued has finished, and allocates no device memory.
  *  - Workspace contract: a workspace must be zero-filled once before its
- *    first use (dsa_workspace_init, or any zero fill).  Every call restores
- *    the counters and histograms it used to zero before its work completes,
- *    so a workspace can be reused call after call with no clearing in
- *    between (which keeps the hot path free of fill kernels and memsets).
- *    After a DSA_ERR_LAUNCH, zero-fill it again.
- *  - Work is enqueued on the caller's stream; calls return without waiting.
+ *    first use (dsa_workspace_init, or any zero fill).  Its first sixteenth
+ *    (rounded down to whole 16 KiB blocks) holds the per-query histograms
+ *    of the top-k; each call accumulates into the first n_q blocks and
+ *    clears them again before its work completes, and puts everything else
+ *    after that region.  So one workspace serves any sequence of calls,
+ *    with any query counts and visible bounds, with no clearing in between
+ *    (a serving loop whose batch size changes step to step keeps one
+ *    workspace), provided that
+ *      (a) every call passes the same ws_bytes (normally the buffer's
+ *          size: the region's extent follows from it), and
+ *      (b) ws_bytes >= dsa_workspace_bytes(geom, n_q, max_nvis) of the call
+ *          (calls that do not fit return DSA_ERR_WORKSPACE).
+ *    After a DSA_ERR_LAUNCH, or after a call that passed another ws_bytes,
+ *    zero-fill it again.
  *    Calls on different streams must use different workspaces.
  *  - Errors: every entry point validates its arguments before enqueuing
  *    anything and returns a status.  On DSA_ERR_ARG, DSA_ERR_UNSUPPORTED,
@@ -116,7 +124,9 @@ typedef struct {
 
 /* Bytes of workspace that dsa_topk, dsa_mla_attend and dsa_decode_step need
  * for this geometry, query count and visible bound (the maximum of the three;
- * one workspace serves all of them).  Returns 0 for an unsupported geometry
+ * one workspace serves all of them): at least 16 x n_q x 16 KiB, so that the
+ * histogram region (the first sixteenth) holds n_q histograms, and large
+ * enough that the rest fits after that region.  Returns 0 for an unsupported geometry
  * or sizes out of range (n_q outside 1..65535, max_nvis outside 1..2^31 - 1). */
 size_t dsa_workspace_bytes(const dsa_geometry *geom, int32_t n_q, int64_t max_nvis);
 

@@ -84,6 +84,17 @@ int oracle_max_threads(void)
 #endif
 }
 
+/* Thread count of the parallel loops that follow (timing only: results do
+ * not depend on it). */
+void oracle_set_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Indexer score of every visible row ([PC] "The Lightning Indexer": a
  * rectified dot product per indexer head, then a weighted sum across heads;

@@ -40,6 +40,8 @@ def load(path: str):
     L.oracle_decode_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f32, i32, i32,
                                      P, P, P, i64, P, P, i64, P, i32, P, P, P, i32]
     L.oracle_max_threads.argtypes = []
+    L.oracle_set_threads.argtypes = [i32]
+    L.oracle_set_threads.restype = None
     L.oracle_pool_append.argtypes = [i32, P, P, P, i64, i32, P, P, i64, P]
     L.oracle_absorb_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
     L.oracle_project_output.argtypes = [i32, i32, i32, i32, P, P, P]
@@ -74,6 +76,11 @@ def _c(a, dtype):
 
 def max_threads(L=None) -> int:
     return int((L or lib()).oracle_max_threads())
+
+
+def set_threads(n: int, L=None) -> None:
+    """Thread count of the oracle's OpenMP loops from now on (timing only)."""
+    (L or lib()).oracle_set_threads(int(n))
 
 
 def index_scores(q_seq, q_nvis, kpool, idx_q, idx_w, idx_k, score_ld=None, fill=np.nan, L=None,

@@ -1,7 +1,7 @@
 """The five problem configurations and the 128K decode point at full size,
 in the launch configuration the benchmark times (the fused step).  The
-oracle checks every query where it finishes in seconds (C0, C1, C2, C4,
-128K) and a sample of positions of the prefill chunk (C3)."""
+oracle checks every query of every configuration, including all 512
+positions of the prefill chunk (C3)."""
 from __future__ import annotations
 
 import time
@@ -43,9 +43,10 @@ def test_config_full(name):
     _run(name)
 
 
-def test_config_c3_sampled():
-    w, sel_g, cnt_g = _run("c3", queries=[0, 1, 2, 127, 255, 256, 383, 509, 510, 511])
-    # every query keeps exactly top_k of its own visible prefix, ascending
+def test_config_c3_full():
+    """Every one of the 512 prefill positions against the oracle (about 20 s
+    of oracle time on 16 host threads)."""
+    w, sel_g, cnt_g = _run("c3")
     for j in range(w.n_q):
         s = sel_g[j, :cnt_g[j]]
         assert cnt_g[j] == 2048 and np.all(np.diff(s) > 0) and s[-1] < w.q_nvis[j]
