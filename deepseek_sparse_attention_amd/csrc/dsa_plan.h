@@ -148,13 +148,19 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     return p;
 }
 
-// Smallest workspace for the plan: the histogram region must hold n_q
-// histograms (ws / 16 >= n_q * 16 KiB) and the body must fit after it
-// (ws - ws / 16 >= body).
+// Smallest workspace for the plan: with k = the histograms its first
+// sixteenth holds (k = ws / 256 KiB, rounded down), k >= n_q and
+// k * 16 KiB + body <= ws.  Growing ws for the body can raise k, which the
+// loop follows until both hold.
 inline size_t workspace_bytes(const Plan &p) {
-    const size_t h = (size_t)p.n_q * kHistQueryBytes * 16;
-    const size_t b = (p.body * 16 + 14) / 15;
-    return align256(h > b ? h : b);
+    size_t k = (size_t)p.n_q;
+    for (;;) {
+        const size_t h = k * kHistQueryBytes * 16, b = k * kHistQueryBytes + p.body;
+        const size_t w = align256(h > b ? h : b);
+        const size_t kk = w / (kHistQueryBytes * 16);
+        if (kk <= k) return w;
+        k = kk;
+    }
 }
 
 // Lays the plan out in a workspace of ws_bytes; false if it does not fit.

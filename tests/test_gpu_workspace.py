@@ -44,9 +44,6 @@ def test_workspace_reused_across_batch_shapes():
     dev = torch.device("cuda")
     cache = torch.from_numpy(w.cache).to(dev)
     idx_k = torch.from_numpy(w.idx_k).to(dev)
-    q_all = torch.from_numpy(w.q).to(dev)
-    iq_all = torch.from_numpy(w.idx_q).to(dev)
-    iw_all = torch.from_numpy(w.idx_w).to(dev)
     ws = B.new_workspace(g, 8, T, device=dev)
     H = hist_region(ws.numel())
     assert H >= 8 * 16384
@@ -59,7 +56,9 @@ def test_workspace_reused_across_batch_shapes():
         q_seq = torch.from_numpy(qs).to(dev)
         q_nvis = torch.from_numpy(nv).to(dev)
         # query j of this call is the workload's query of its sequence
-        q, iq, iw = q_all[q_seq.long()].contiguous(), iq_all[q_seq.long()].contiguous(), iw_all[q_seq.long()].contiguous()
+        q = torch.from_numpy(np.ascontiguousarray(w.q[qs])).to(dev)
+        iq = torch.from_numpy(np.ascontiguousarray(w.idx_q[qs])).to(dev)
+        iw = torch.from_numpy(np.ascontiguousarray(w.idx_w[qs])).to(dev)
         sel = torch.full((n_q, sel_ld), -7, dtype=torch.int32, device=dev)
         cnt = torch.empty(n_q, dtype=torch.int32, device=dev)
         out = torch.empty((n_q, g["n_heads"], g["d_latent"]), dtype=torch.float32, device=dev)
