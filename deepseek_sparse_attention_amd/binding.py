@@ -30,7 +30,7 @@ class Batch(ctypes.Structure):
 EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_index_scores", "dsa_topk", "dsa_mla_attend",
            "dsa_decode_step", "dsa_pool_append", "dsa_absorb_query", "dsa_project_output", "dsa_index_prepare",
            "dsa_status_str", "dsa_last_error", "dsa_device_check", "dsa_set_timing_events", "dsa_timing_ran",
-           "dsa_stream_read")
+           "dsa_stream_read", "dsa_decode_step_noalloc")
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -46,6 +46,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "dsa_topk": (ctypes.c_int, [G, B, P, i64, P, i32, P, P, sz, P]),
         "dsa_mla_attend": (ctypes.c_int, [G, B, P, P, i64, P, i32, P, P, P, P, sz, P]),
         "dsa_decode_step": (ctypes.c_int, [G, B, P, P, P, i64, P, P, i64, P, i32, P, P, P, P, sz, P]),
+        "dsa_decode_step_noalloc": (ctypes.c_int, [G, B, P, P, P, i64, P, P, i64, P, i32, P, P, P, P]),
         "dsa_pool_append": (ctypes.c_int, [i32, P, P, i32, P, i64, P, P, i64, P, P]),
         "dsa_absorb_query": (ctypes.c_int, [i32, i32, P, P, P, P, P]),
         "dsa_project_output": (ctypes.c_int, [i32, P, P, P, P]),
@@ -148,6 +149,15 @@ def decode_step(geom: dict, b: Batch, idx_q, idx_w, idx_k, key_seq_stride: int, 
                                 _ptr(idx_k), int(key_seq_stride), _ptr(q), _ptr(cache), int(cache_seq_stride),
                                 _ptr(sel), int(sel_ld), _ptr(sel_count), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream)), "dsa_decode_step")
+
+
+def decode_step_noalloc(geom: dict, b: Batch, idx_q, idx_w, idx_k, key_seq_stride: int, q, cache,
+                        cache_seq_stride: int, sel, sel_ld: int, sel_count, out, lse, stream=None) -> None:
+    """The fused step on the library's own device scratch (no workspace)."""
+    _check(_lib.dsa_decode_step_noalloc(ctypes.byref(geometry(geom)), ctypes.byref(b), _ptr(idx_q), _ptr(idx_w),
+                                        _ptr(idx_k), int(key_seq_stride), _ptr(q), _ptr(cache),
+                                        int(cache_seq_stride), _ptr(sel), int(sel_ld), _ptr(sel_count), _ptr(out),
+                                        _ptr(lse), _stream(stream)), "dsa_decode_step_noalloc")
 
 
 def pool_append(n_tok, n_new, max_new: int, new_kg, rolling, pool_keys, pos_emb, stream=None) -> None:

@@ -29,7 +29,11 @@ hipError_t launch_pool_append(const PoolArgs &a, hipStream_t st);
 hipError_t launch_absorb(const AbsorbArgs &a, hipStream_t st);
 hipError_t launch_project(const AbsorbArgs &a, hipStream_t st);
 hipError_t launch_index_prep(const PrepArgs &a, hipStream_t st);
+hipError_t scratch_acquire(hipStream_t st, void **ptr);
+void scratch_mark_dirty();
 }  // namespace dsa
+
+static_assert(DSA_NOALLOC_SCRATCH_BYTES == dsa::kScratchBytes, "scratch size in the header and the library agree");
 
 namespace {
 
@@ -317,60 +321,112 @@ int dsa_mla_attend(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *q,
     });
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the fused step that do not concern the workspace; the
+// plan is made here.
+int check_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *idx_q, const float *idx_w,
+               const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q, const dsa_bf16 *cache,
+               int64_t cache_seq_stride, const int32_t *sel, int32_t sel_ld, const int32_t *sel_count,
+               const float *out, const float *lse, dsa::Plan &p) {
+    DSA_TRY(check_geometry(g));
+    DSA_TRY(check_batch(b));
+    if (!idx_q || !idx_w || !idx_k || !q || !cache || !out) return fail(DSA_ERR_ARG, "NULL tensor pointer");
+    if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(idx_k) || !aligned16(q) || !aligned16(cache) ||
+        !aligned16(out) || (lse && !aligned16(lse)) || (sel && !aligned16(sel)) ||
+        (sel_count && !aligned16(sel_count)))
+        return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if ((sel == nullptr) != (sel_count == nullptr)) return fail(DSA_ERR_ARG, "sel and sel_count go together");
+    p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
+    if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
+    if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
+    if (sel && sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
+    return DSA_OK;
+}
+
+// Enqueues the fused step on a plan already placed in the workspace ws.
+int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, const dsa_bf16 *idx_q,
+                 const float *idx_w, const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q,
+                 const dsa_bf16 *cache, int64_t cache_seq_stride, int32_t *sel, int32_t sel_ld, int32_t *sel_count,
+                 float *out, float *lse, void *ws, hipStream_t stream) {
+    dsa::Args a = base_args(g, b, p);
+    bind_workspace(a, p, ws);
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    a.idx_q = idx_q;
+    a.idx_w = idx_w;
+    a.idx_k = idx_k;
+    a.key_stride = key_seq_stride;
+    a.scores = reinterpret_cast<float *>(w + p.off_scores);
+    a.scores_in = a.scores;
+    a.score_ld = p.score_ld;
+    a.q = q;
+    a.cache = cache;
+    a.cache_stride = cache_seq_stride;
+    if (sel) {
+        a.sel = sel;
+        a.sel_ld = sel_ld;
+        a.sel_count = sel_count;
+    } else {
+        a.sel = reinterpret_cast<int32_t *>(w + p.off_sel);
+        a.sel_ld = p.sel_max;
+        a.sel_count = reinterpret_cast<int32_t *>(w + p.off_cnt);
+    }
+    a.out = out;
+    a.lse = lse;
+    a.fused = 1;
+    hipEvent_t ev[10];
+    for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
+    g_ran = 0;
+    DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream, ev[0], ev[1]), "score"));
+    if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
+    DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
+    DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
+    g_ran = 1 | (a.select_scan ? 0 : 2) | 4 | 8 | (a.n_split > 1 ? 16 : 0);
+    return (int)DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int dsa_decode_step(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *idx_q, const float *idx_w,
                     const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q, const dsa_bf16 *cache,
                     int64_t cache_seq_stride, int32_t *sel, int32_t sel_ld, int32_t *sel_count, float *out,
                     float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
     return guarded([&] {
         DSA_TRY(check_device());
-        DSA_TRY(check_geometry(g));
-        DSA_TRY(check_batch(b));
-        if (!idx_q || !idx_w || !idx_k || !q || !cache || !out) return fail(DSA_ERR_ARG, "NULL tensor pointer");
-        if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(idx_k) || !aligned16(q) || !aligned16(cache) ||
-            !aligned16(out) || (lse && !aligned16(lse)) || (sel && !aligned16(sel)) ||
-            (sel_count && !aligned16(sel_count)))
-            return fail(DSA_ERR_ARG, "tensor pointers must be 16-byte aligned");
-        if ((sel == nullptr) != (sel_count == nullptr)) return fail(DSA_ERR_ARG, "sel and sel_count go together");
-        dsa::Plan p = dsa::make_plan(g->kpool, g->top_k, g->d_rope, b->n_q, b->max_nvis);
-        if (key_seq_stride < p.max_rows) return fail(DSA_ERR_ARG, "key_seq_stride < max_nvis / kpool");
-        if (cache_seq_stride < b->max_nvis) return fail(DSA_ERR_ARG, "cache_seq_stride < max_nvis");
-        if (sel && sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
+        dsa::Plan p;
+        DSA_TRY(check_step(g, b, idx_q, idx_w, idx_k, key_seq_stride, q, cache, cache_seq_stride, sel, sel_ld,
+                           sel_count, out, lse, p));
         DSA_TRY(check_ws(p, ws, ws_bytes));
         if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
-        dsa::Args a = base_args(g, b, p);
-        bind_workspace(a, p, ws);
-        uint8_t *w = static_cast<uint8_t *>(ws);
-        a.idx_q = idx_q;
-        a.idx_w = idx_w;
-        a.idx_k = idx_k;
-        a.key_stride = key_seq_stride;
-        a.scores = reinterpret_cast<float *>(w + p.off_scores);
-        a.scores_in = a.scores;
-        a.score_ld = p.score_ld;
-        a.q = q;
-        a.cache = cache;
-        a.cache_stride = cache_seq_stride;
-        if (sel) {
-            a.sel = sel;
-            a.sel_ld = sel_ld;
-            a.sel_count = sel_count;
-        } else {
-            a.sel = reinterpret_cast<int32_t *>(w + p.off_sel);
-            a.sel_ld = p.sel_max;
-            a.sel_count = reinterpret_cast<int32_t *>(w + p.off_cnt);
-        }
-        a.out = out;
-        a.lse = lse;
-        a.fused = 1;
-        hipEvent_t ev[10];
-        for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
-        g_ran = 0;
-        DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream, ev[0], ev[1]), "score"));
-        if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
-        DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
-        DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
-        g_ran = 1 | (a.select_scan ? 0 : 2) | 4 | 8 | (a.n_split > 1 ? 16 : 0);
-        return (int)DSA_OK;
+        return enqueue_step(g, b, p, idx_q, idx_w, idx_k, key_seq_stride, q, cache, cache_seq_stride, sel, sel_ld,
+                            sel_count, out, lse, ws, stream);
+    });
+}
+
+int dsa_decode_step_noalloc(const dsa_geometry *g, const dsa_batch *b, const dsa_bf16 *idx_q, const float *idx_w,
+                            const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q, const dsa_bf16 *cache,
+                            int64_t cache_seq_stride, int32_t *sel, int32_t sel_ld, int32_t *sel_count, float *out,
+                            float *lse, hipStream_t stream) {
+    return guarded([&] {
+        DSA_TRY(check_device());
+        dsa::Plan p;
+        DSA_TRY(check_step(g, b, idx_q, idx_w, idx_k, key_seq_stride, q, cache, cache_seq_stride, sel, sel_ld,
+                           sel_count, out, lse, p));
+        if (!dsa::place_workspace(p, dsa::kScratchBytes))
+            return fail(DSA_ERR_WORKSPACE, "the call needs a workspace of " + std::to_string(dsa::workspace_bytes(p)) +
+                                               " bytes; the allocation-free entry point's scratch holds " +
+                                               std::to_string(dsa::kScratchBytes));
+        if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        void *ws = nullptr;
+        DSA_TRY(launched(dsa::scratch_acquire(stream, &ws), "scratch"));
+        const int s = enqueue_step(g, b, p, idx_q, idx_w, idx_k, key_seq_stride, q, cache, cache_seq_stride, sel,
+                                   sel_ld, sel_count, out, lse, ws, stream);
+        if (s != DSA_OK) dsa::scratch_mark_dirty();
+        return s;
     });
 }
 

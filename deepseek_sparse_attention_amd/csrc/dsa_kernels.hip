@@ -2513,3 +2513,54 @@ hipError_t launch_index_prep(const PrepArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 }  // namespace dsa
+
+// ---------------------------------------------------------------- scratch of the allocation-free step
+// The workspace of dsa_decode_step_noalloc: a file-scope device array that
+// each GPU the library runs on holds from module load until the process
+// ends.  In host code the name `scratch` is only a stand-in for the array,
+// never its device address: host code uses the address hipGetSymbolAddress
+// returns, looked up once per device with that device current and kept per
+// device.  Only its histogram region (the first sixteenth) must start at
+// zero; every call leaves it zero again, and the first use on a device (or
+// the first after a failed launch) clears it with a fill kernel.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[dsa::kScratchBytes];
+
+#include <mutex>
+
+namespace dsa {
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kScratchDevices];        // device address of each device's copy
+bool g_scratch_clear[kScratchDevices];   // its histogram region is known to be zero
+}  // namespace
+
+hipError_t scratch_acquire(hipStream_t st, void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    if (!g_scratch_clear[dev]) {
+        e = launch_fill_zero(g_scratch[dev], hist_region_bytes(kScratchBytes), st);
+        if (e != hipSuccess) return e;
+        g_scratch_clear[dev] = true;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
+}
+
+void scratch_mark_dirty() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch_clear[dev] = false;
+}
+}  // namespace dsa

@@ -18,6 +18,8 @@ constexpr int kMaxChunks = 1024;  // top-k chunks per query (one per k_select th
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
 constexpr int kMaxSplitRows = 4096;  // selected rows per attention work-group
 constexpr int kWvMaxRows = 2048;     // the same for k_attend_wv
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // workspace of the allocation-free fused step
+                                                    // (DSA_NOALLOC_SCRATCH_BYTES)
 
 // Everything a launch needs that depends on (geometry, n_q, max_nvis).
 struct Plan {

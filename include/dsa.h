@@ -194,6 +194,28 @@ int dsa_decode_step(const dsa_geometry *geom, const dsa_batch *batch,
                     float *out, float *lse,
                     void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The fused step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and errors as dsa_decode_step, without the
+ * workspace: the call uses the library's own device scratch of
+ * DSA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, a static array that each GPU
+ * holds from the library's load until the process ends.  A call whose
+ * workspace would not fit in it (dsa_workspace_bytes above that size; the
+ * 8 x 131,072-token decode needs about 16 MB) returns DSA_ERR_WORKSPACE
+ * before enqueuing anything.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks up that device's copy of the array and clears its histogram
+ * region with a fill kernel on the stream.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dsa_decode_step_noalloc(const dsa_geometry *geom, const dsa_batch *batch,
+                            const dsa_bf16 *idx_q, const float *idx_w,
+                            const dsa_bf16 *idx_k, int64_t key_seq_stride,
+                            const dsa_bf16 *q, const dsa_bf16 *cache, int64_t cache_seq_stride,
+                            int32_t *sel, int32_t sel_ld, int32_t *sel_count,
+                            float *out, float *lse, hipStream_t stream);
+
 /* 5. k-pool key producer ("GLM-5.3-Flash on WASTE", "DeepSeek Sparse
  * Attention, k-pool flavour"; TensorSharp2 "GLM-5.3-Flash (glm5next)").
  * A cell is a token's indexer key followed by its gate, 2 x 128 bf16.
