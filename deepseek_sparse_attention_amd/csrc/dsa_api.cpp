@@ -376,14 +376,21 @@ int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, 
     a.out = out;
     a.lse = lse;
     a.fused = 1;
+    // decode batches select inside the attention (k_attend_sel); a prefill
+    // chunk keeps k_select
+    a.attn_sel = p.attn_sel && !a.prefill ? 1 : 0;
+    a.sel_export = sel ? 1 : 0;
+    // the scorer's histograms feed k_filter, or k_select's own scan; the
+    // in-attention scan builds its own
+    a.hist_on = (a.attn_sel && a.select_scan) ? 0 : 1;
     hipEvent_t ev[10];
     for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
     g_ran = 0;
     DSA_TRY(launched(dsa::launch_score(a, p.max_rows, stream, ev[0], ev[1]), "score"));
     if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream, ev[2], ev[3]), "filter"));
-    DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
+    if (!a.attn_sel) DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
     DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
-    g_ran = 1 | (a.select_scan ? 0 : 2) | 4 | 8 | (a.n_split > 1 ? 16 : 0);
+    g_ran = 1 | (a.select_scan ? 0 : 2) | (a.attn_sel ? 0 : 4) | 8 | (a.n_split > 1 ? 16 : 0);
     return (int)DSA_OK;
 }
 

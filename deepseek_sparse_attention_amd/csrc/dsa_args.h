@@ -43,6 +43,9 @@ struct Args {
     int32_t idx_f16;      // indexer queries and keys are IEEE f16 (else bf16)
     int32_t attn_hs;      // attention kernel: 0 k_attend, 1 k_attend_hs, 2 k_attend_wv
     int32_t select_scan;  // k_select gathers its candidates itself (no k_filter)
+    int32_t attn_sel;     // fused step: the top-k runs inside the attention (k_attend_sel)
+    int32_t hist_on;      // the scorer accumulates the first-digit histograms
+    int32_t sel_export;   // k_attend_sel writes the selection and its count to sel / sel_count
 };
 
 // Arguments of the k-pool key producer.

@@ -133,23 +133,18 @@ __device__ uint32_t block_sum(uint32_t v, uint32_t *smem) {
     return total;
 }
 
-// Radix step: with hist[0..NB) of the items still in play and `need` of
-// them still to take from the top, find the bin b holding the need-th
-// largest: suffix(b) >= need > suffix(b+1).  Returns b, sets above =
-// suffix(b+1).  256 threads; thread t owns the PER bins just below
-// NB - PER*t, kept in registers.
-template <int NB>
-__device__ uint32_t find_bucket(const uint32_t *hist, uint32_t need, uint32_t *smem, uint32_t *res,
-                                uint32_t &above) {
-    constexpr int PER = NB / 256;
-    const int hi = NB - PER * (int)threadIdx.x;
-    uint32_t c[PER];
+// Radix step: with the counts of NB = 256 PER bins of the items still in
+// play and `need` of them still to take from the top, find the bin b
+// holding the need-th largest: suffix(b) >= need > suffix(b+1).  Returns b,
+// sets above = suffix(b+1).  256 threads; thread t holds in c the counts of
+// the PER bins just below NB - PER*t (c[i]: bin NB - PER t - 1 - i).
+template <int PER>
+__device__ uint32_t bucket_from_regs(const uint32_t (&c)[PER], uint32_t need, uint32_t *smem, uint32_t *res,
+                                     uint32_t &above) {
+    const int hi = 256 * PER - PER * (int)threadIdx.x;
     uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-        c[i] = hist[hi - 1 - i];
-        s += c[i];
-    }
+    for (int i = 0; i < PER; i++) s += c[i];
     uint32_t total;
     const uint32_t before = block_excl_scan(s, smem, total);   // items in higher bins
     if (before < need && before + s >= need) {
@@ -172,6 +167,18 @@ __device__ uint32_t find_bucket(const uint32_t *hist, uint32_t need, uint32_t *s
     const uint32_t b = res[0];
     __syncthreads();
     return b;
+}
+
+// The same over a histogram hist[0..NB) in memory.
+template <int NB>
+__device__ uint32_t find_bucket(const uint32_t *hist, uint32_t need, uint32_t *smem, uint32_t *res,
+                                uint32_t &above) {
+    constexpr int PER = NB / 256;
+    const int hi = NB - PER * (int)threadIdx.x;
+    uint32_t c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) c[i] = hist[hi - 1 - i];
+    return bucket_from_regs<PER>(c, need, smem, res, above);
 }
 
 // Reductions over lanes l and l ^ 16 (l ^ 32) with v_permlane16_swap
@@ -289,10 +296,17 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
         drain();
         return;
     }
-    const bool hist = a.fused != 0;
+    const bool hist = a.hist_on != 0;
     if (hist) {
         for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
         __syncthreads();
+    }
+    // the in-attention top-k: k_filter accumulates the second-digit
+    // histogram of the threshold bucket, which must start at zero; the
+    // query's first work-group clears it (what the last call left there)
+    if (!STRIDE && a.attn_sel && !a.select_scan && blockIdx.x == 0) {
+        uint32_t *h2 = a.hist + (size_t)q * kHistStride + kHistH2;
+        for (int i = threadIdx.x; i < 1024; i += 256) h2[i] = 0;
     }
 
     bf16x8 qa[2][4];
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     }
     if (hist) {
         __syncthreads();
-        uint32_t *gh = a.hist + (size_t)q * kHistBins;
+        uint32_t *gh = a.hist + (size_t)q * kHistStride;
         for (int i = threadIdx.x; i < kHistBins; i += 256)
             if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
     }
@@ -414,7 +428,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_score_prefill(Args a) {
     const int sl = w % (kPfWaves / P);       // and its share of each tile
     const int q = q0 + slot;
     const int lead = query_seq(a, q0);
-    const bool hist = a.fused != 0;
+    const bool hist = a.hist_on != 0;
     // does each query slot take part, and up to which row
     if (threadIdx.x < kPfQ) {
         int32_t rr = 0;
@@ -557,7 +571,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_score_prefill(Args a) {
             const uint32_t word = (&lh[0][0])[i];
             if (!word || qq >= q_end) continue;
             const int bin = 2 * (i % (kHistBins / 2));
-            uint32_t *gh = a.hist + (size_t)qq * kHistBins + bin;
+            uint32_t *gh = a.hist + (size_t)qq * kHistStride + bin;
             if (word & 0xFFFFu) atomicAdd(gh, word & 0xFFFFu);
             if (word >> 16) atomicAdd(gh + 1, word >> 16);
         }
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
     const float *s = a.scores_in + (size_t)q * a.score_ld;
     for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) atomicAdd(&lhist[order_key(s[r]) >> 20], 1u);
     __syncthreads();
-    uint32_t *gh = a.hist + (size_t)q * kHistBins;
+    uint32_t *gh = a.hist + (size_t)q * kHistStride;
     for (int i = threadIdx.x; i < kHistBins; i += 256)
         if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
 }
@@ -647,7 +661,7 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     // first block of scores in flight while the threshold bucket is found
     float sv[8];
     load_scores<8>(s, r0 + 8 * threadIdx.x, r1, vec, sv);
-    load_hist(a.hist + (size_t)q * kHistBins, hist);
+    load_hist(a.hist + (size_t)q * kHistStride, hist);
     __syncthreads();
     uint32_t above1;
     const uint32_t b1 = find_bucket<kHistBins>(hist, (uint32_t)a.keep, scan, res, above1);
@@ -657,6 +671,7 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
     }
 
     uint64_t *slots = a.cand + ((size_t)q * a.n_chunks + c) * a.cand_cap;
+    uint32_t *h2 = a.attn_sel ? a.hist + (size_t)q * kHistStride + kHistH2 : nullptr;
     uint32_t n_cand = 0;
     for (int64_t sb = r0; sb < r1; sb += 2048) {
         const int64_t rb = sb + 8 * threadIdx.x;
@@ -676,6 +691,9 @@ __global__ __launch_bounds__(256) void k_filter(Args a) {
             if (!((m >> i) & 1)) continue;
             if (pos < (uint32_t)a.cand_cap) slots[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)(rb + i);
             pos++;
+            // the in-attention selection takes the second digit of the
+            // threshold bucket's rows from this histogram
+            if (h2 && (keys[i] >> 20) == b1) atomicAdd(&h2[(keys[i] >> 10) & 1023], 1u);
         }
     }
     if (threadIdx.x == 0) a.chunk_cnt[(size_t)q * a.n_chunks + c] = n_cand;
@@ -766,7 +784,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Args a) {
     // read before it clears them
     uint32_t c1[kHistBins / kSelThreads];
     {
-        uint32_t *gh = a.hist + (size_t)q * kHistBins;
+        uint32_t *gh = a.hist + (size_t)q * kHistStride;
         if (SCAN) {
 #pragma unroll
             for (int i = 0; i < kHistBins / kSelThreads; i++) c1[i] = gh[kHistBins - 1 - 4 * tid - i];
@@ -1124,8 +1142,14 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
-// The same with a uniform base address in SGPRs and a per-lane 32-bit offset.
-__device__ __forceinline__ void dma16s(const void *base, uint32_t off, uint32_t lds) {
+// The same with a uniform base address in SGPRs and a per-lane 32-bit offset
+// (the base is passed through readfirstlane, which keeps it in SGPRs for the
+// asm operand wherever the compiler cannot prove it uniform).
+__device__ __forceinline__ void dma16s(const void *base_in, uint32_t off, uint32_t lds) {
+    const uint64_t bi = reinterpret_cast<uint64_t>(base_in);
+    const uint64_t bu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bi) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bi >> 32)) << 32);
+    const void *base = reinterpret_cast<const void *>(bu);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -1634,61 +1658,16 @@ struct WvCfg {
 };
 static_assert(4 * 16 * WvCfg<512>::OS * 4 <= 4 * WvCfg<512>::WAVE, "merge fits the row buffers");
 
+// Row loop and merge of the wave-private attention, shared by k_attend_wv
+// and k_attend_sel.  On entry sidx holds the split's row indices, wave w's
+// step j in sidx[16 (w + 4 j) .. + 15] (-1: no row), nj is this wave's step
+// count, and qreg holds the wave's queries (their loads may be in flight).
 template <int D>
-__global__ __launch_bounds__(256) void k_attend_wv(Args a) {
+__device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32_t *sidx, float (*smx)[16],
+                                        float (*ssum)[16], const bf16x8 (&qreg)[WvCfg<D>::ND], const uint8_t *C,
+                                        int q, int sp, int hg, int w, int nj, bool invalid) {
     using Cfg = WvCfg<D>;
-    constexpr int kPer = kWvMaxRows / 256;                  // row indices per thread
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Cfg::WAVE];
-    __shared__ int32_t sidx[kWvMaxRows];
-    __shared__ float smx[4][16], ssum[4][16];
-    const int pairs = a.n_q * a.n_split;
-    const int pairs8 = (pairs + 7) & ~7;
-    const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
-    if (pair >= pairs) return;
-    const int q = pair / a.n_split, sp = pair % a.n_split;
-    const int32_t count_in = a.sel_count[q];   // issued with the query's own loads
-    const QInfo qi = query_info(a, q);
     const int lane = lane_id(), g = lane >> 4, n = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int head = 16 * hg + n;
-    const int32_t start = sp * a.split_rows;
-
-    // The count, the split's row indices and the queries are loaded in one
-    // round trip; indices past the count are read (inside the caller's row
-    // stride) and dropped once the count is known.  Wave w reads the indices
-    // of its own steps w, w + 4, ...: lane l of rix[i] holds row l & 15 of
-    // the wave's step 4 i + l / 16, and the wave keeps them in its own part
-    // of sidx, so no barrier is needed before its first DMA.
-    int32_t rix[kPer];
-    {
-        const int32_t *selq = a.sel + (size_t)q * a.sel_ld + start;
-#pragma unroll
-        for (int i = 0; i < kPer; i++) {
-            const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
-            rix[i] = (r < a.split_rows && start + r < a.sel_ld) ? selq[r] : -1;
-        }
-    }
-    bf16x8 qreg[Cfg::ND];
-    {
-        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 8 * g;
-#pragma unroll
-        for (int j = 0; j < Cfg::ND; j++) qreg[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j));
-    }
-    // a count outside [0, top_k + kpool - 1] makes the query invalid
-    const bool invalid = qi.mode == 2 || count_in < 0 || count_in > a.top_k + a.kpool - 1;
-    const int32_t count = invalid ? 0 : count_in;
-    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
-    const int nst = (nrows + kWvRows - 1) / kWvRows;
-    const int nj = nst > w ? (nst - w + 3) / 4 : 0;   // this wave's steps w, w + 4, ...
-    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-        const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
-        int32_t t = rix[i];
-        if (r >= nrows || t < 0 || (int64_t)t >= a.cache_stride) t = -1;
-        if (4 * i + g < nj) sidx[r] = t;
-    }
-
     uint8_t *wb = lds + w * Cfg::WAVE;
     const uint32_t voff = 16 * lane;
     const uint32_t wb_lds = __builtin_amdgcn_readfirstlane(lds_addr(wb));
@@ -1885,6 +1864,454 @@ __global__ __launch_bounds__(256) void k_attend_wv(Args a) {
             }
         }
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attend_wv(Args a) {
+    using Cfg = WvCfg<D>;
+    constexpr int kPer = kWvMaxRows / 256;                  // row indices per thread
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Cfg::WAVE];
+    __shared__ int32_t sidx[kWvMaxRows];
+    __shared__ float smx[4][16], ssum[4][16];
+    const int pairs = a.n_q * a.n_split;
+    const int pairs8 = (pairs + 7) & ~7;
+    const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
+    if (pair >= pairs) return;
+    const int q = pair / a.n_split, sp = pair % a.n_split;
+    const int32_t count_in = a.sel_count[q];   // issued with the query's own loads
+    const QInfo qi = query_info(a, q);
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int head = 16 * hg + n;
+    const int32_t start = sp * a.split_rows;
+
+    // The count, the split's row indices and the queries are loaded in one
+    // round trip; indices past the count are read (inside the caller's row
+    // stride) and dropped once the count is known.  Wave w reads the indices
+    // of its own steps w, w + 4, ...: lane l of rix[i] holds row l & 15 of
+    // the wave's step 4 i + l / 16, and the wave keeps them in its own part
+    // of sidx, so no barrier is needed before its first DMA.
+    int32_t rix[kPer];
+    {
+        const int32_t *selq = a.sel + (size_t)q * a.sel_ld + start;
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
+            rix[i] = (r < a.split_rows && start + r < a.sel_ld) ? selq[r] : -1;
+        }
+    }
+    bf16x8 qreg[Cfg::ND];
+    {
+        const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 8 * g;
+#pragma unroll
+        for (int j = 0; j < Cfg::ND; j++) qreg[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j));
+    }
+    // a count outside [0, top_k + kpool - 1] makes the query invalid
+    const bool invalid = qi.mode == 2 || count_in < 0 || count_in > a.top_k + a.kpool - 1;
+    const int32_t count = invalid ? 0 : count_in;
+    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
+    const int nst = (nrows + kWvRows - 1) / kWvRows;
+    const int nj = nst > w ? (nst - w + 3) / 4 : 0;   // this wave's steps w, w + 4, ...
+    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        const int r = kWvRows * (w + 4 * (4 * i + g)) + n;
+        int32_t t = rix[i];
+        if (r >= nrows || t < 0 || (int64_t)t >= a.cache_stride) t = -1;
+        if (4 * i + g < nj) sidx[r] = t;
+    }
+
+    wv_rows<D>(a, lds, sidx, smx, ssum, qreg, C, q, sp, hg, w, nj, invalid);
+}
+
+// ---------------------------------------------------------------- top-k inside the attention work-group
+// k_attend_sel: the wave-private attention of k_attend_wv with the exact
+// top-k (same definition as k_select) done by every attention work-group
+// of the query itself, in LDS, before its rows are fetched: no k_select
+// launch, and no selection written to and read back from memory.  The
+// work-group takes the candidates of the query (k_filter's chunk slots, or
+// in SCAN mode, rows of at most 16,384, every row whose first digit reaches
+// the threshold bucket of a histogram it builds itself), resolves digits 2
+// and 3 of the keep-th order key, ranks the kept rows in ascending row
+// order, and keeps the token positions of its own split.  The candidate
+// arrays alias the row buffers, which are free until the first DMA.  When
+// the candidates exceed the LDS, the same decisions are made from passes
+// over the query's scores.
+constexpr int kAsCap = 12288;            // candidates kept in LDS
+constexpr int kAsPer = 16;               // rows per thread per pass tile
+constexpr int kAsTile = 256 * kAsPer;
+
+struct AsShared {
+    uint64_t kr[kAsCap];                 // candidates in row order: order key << 32 | row
+    uint32_t pre[kMaxChunks + 1];        // exclusive prefix of the chunks' candidate counts
+    uint32_t h1[kHistBins];              // first digit (SCAN mode)
+    uint32_t h2[1024];
+    uint32_t h3[1024];
+    uint32_t scan[4];
+    uint32_t res[4];
+};
+static_assert(sizeof(AsShared) <= 4 * WvCfg<512>::WAVE, "the selection fits the row buffers");
+
+// Copies every row r in [r0, r1) whose first digit is at least b1 as (key,
+// r), in row order, to sh.key / sh.row from position `base` on; entries at
+// or past `limit` are counted but not stored.  Returns the number found.
+__device__ __forceinline__ uint32_t as_compact(const float *s, bool vec, int64_t r0, int64_t r1, uint32_t b1, uint32_t base,
+                               uint32_t limit, AsShared &sh) {
+    uint32_t found = 0;
+    for (int64_t sb = r0; sb < r1; sb += kAsTile) {
+        const int64_t rb = sb + kAsPer * threadIdx.x;
+        float v[kAsPer];
+        load_scores<kAsPer>(s, rb, r1, vec, v);
+        uint32_t keys[kAsPer];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kAsPer; i++) {
+            keys[i] = order_key(v[i]);
+            if (rb + i < r1 && (keys[i] >> 20) >= b1) m |= 1u << i;
+        }
+        uint32_t tot;
+        uint32_t pos = base + found + block_excl_scan(__builtin_popcount(m), sh.scan, tot);
+        found += tot;
+#pragma unroll
+        for (int i = 0; i < kAsPer; i++) {
+            if (!((m >> i) & 1)) continue;
+            if (pos < limit) sh.kr[pos] = ((uint64_t)keys[i] << 32) | (uint32_t)(rb + i);
+            pos++;
+        }
+    }
+    return found;
+}
+
+// One pass over rows [0, rows) of the query's scores adding the order keys
+// k with (k >> shift) == match to h[(k >> hshift) & (nb - 1)].
+__device__ __forceinline__ void as_hist_pass(const float *s, bool vec, int64_t rows, int shift, uint32_t match, int hshift,
+                             uint32_t nb, uint32_t *h) {
+    for (int64_t sb = 0; sb < rows; sb += kAsTile) {
+        const int64_t rb = sb + kAsPer * threadIdx.x;
+        float v[kAsPer];
+        load_scores<kAsPer>(s, rb, rows, vec, v);
+#pragma unroll
+        for (int i = 0; i < kAsPer; i++) {
+            const uint32_t k = order_key(v[i]);
+            if (rb + i < rows && (shift >= 32 || (k >> shift) == match)) atomicAdd(&h[(k >> hshift) & (nb - 1)], 1u);
+        }
+    }
+}
+
+// The selection of query q, restricted to token positions [start, start +
+// split_rows): sidx[P - start] = the token at position P of the ascending
+// selection (kept pools expanded, then the unpooled tail), -1 past the
+// count.  With write_sel the same positions go to sel (and, for the last
+// split, the padding after the splits up to sel_ld; for the first split the
+// count).  Returns the selection count.  All 256 threads call it.
+template <bool SCAN, class IssueQ>
+__device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_t *sidx, int q, const QInfo &qi,
+                                             int sp, bool write_sel, IssueQ issue_q) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int kp = a.kpool;
+    const int32_t start = sp * a.split_rows, split_end = start + a.split_rows;
+    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    int32_t count = 0;
+    int32_t pooled = 0, tail = 0;   // sparse: positions [0, pooled) are kept pools, then `tail` tail tokens
+    if (qi.mode != 1) issue_q();
+    // kept row number p (ascending) -> token positions p kp .. p kp + kp - 1
+    auto emit = [&](uint32_t p, int32_t r) {
+#pragma unroll 1
+        for (int j = 0; j < kp; j++) {
+            const int32_t P = (int32_t)p * kp + j;
+            if (P >= start && P < split_end) {
+                const int32_t tok = r * kp + j;
+                sidx[P - start] = tok;
+                if (write_sel && P < a.sel_ld) dst[P] = tok;
+            }
+        }
+    };
+    if (qi.mode == 1) {
+        const uint32_t keep = (uint32_t)a.keep;
+        const int64_t rows = qi.rows;
+        const float *s = a.scores_in + (size_t)q * a.score_ld;
+        const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+        for (int i = tid; i < 1024; i += 256) sh.h3[i] = 0;
+        uint32_t b1, above1, n_cand = 0, b2, above2;
+        bool in_lds;
+        if (SCAN) {
+            issue_q();
+            for (int i = tid; i < kHistBins; i += 256) sh.h1[i] = 0;
+            for (int i = tid; i < 1024; i += 256) sh.h2[i] = 0;
+            __syncthreads();
+            as_hist_pass(s, vec, rows, 32, 0u, 20, kHistBins, sh.h1);
+            __syncthreads();
+            b1 = find_bucket<kHistBins>(sh.h1, keep, sh.scan, sh.res, above1);
+            n_cand = above1 + sh.h1[b1];
+            in_lds = n_cand <= (uint32_t)kAsCap;
+            if (in_lds) {
+                as_compact(s, vec, 0, rows, b1, 0u, (uint32_t)kAsCap, sh);
+                __syncthreads();
+                for (uint32_t i0 = 0; i0 < n_cand; i0 += 256 * 8) {
+                    uint32_t k[8];
+#pragma unroll
+                    for (int u = 0; u < 8; u++) {
+                        const uint32_t i = i0 + tid + 256 * u;
+                        k[u] = i < n_cand ? (uint32_t)(sh.kr[i] >> 32) : 0u;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; u++) {
+                        const uint32_t i = i0 + tid + 256 * u;
+                        if (i < n_cand && (k[u] >> 20) == b1) atomicAdd(&sh.h2[(k[u] >> 10) & 1023], 1u);
+                    }
+                }
+            } else {
+                as_hist_pass(s, vec, rows, 20, b1, 10, 1024, sh.h2);
+            }
+            __syncthreads();
+            b2 = find_bucket<1024>(sh.h2, keep - above1, sh.scan, sh.res, above2);
+        } else {
+            // One round trip brings the threshold bucket b1 and the rows
+            // above it (k_filter), the second-digit histogram of bucket b1
+            // (k_filter's; thread t: bins 1023 - 4t - i), the chunk candidate
+            // counts (thread t: chunks 4t .. 4t + 3; lane l of wave w also
+            // chunk w + 4 (l % 16)), and the first 128 slots of the wave's
+            // chunks w + 4u, read before the counts say how many are filled.
+            // The queries follow.
+            const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+            const uint32_t *cc = a.chunk_cnt + (size_t)q * a.n_chunks;
+            const uint32_t *gh2 = a.hist + (size_t)q * kHistStride + kHistH2;
+            const uint64_t *cq = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
+            constexpr int kU = 16;
+            u32x4 sv[kU];
+#pragma unroll
+            for (int u = 0; u < kU; u++) {
+                const int c = w + 4 * u;
+                sv[u] = c < nch ? *(const u32x4 *)(cq + (size_t)c * a.cand_cap + 2 * lane) : u32x4{0u, 0u, 0u, 0u};
+            }
+            const int cl = w + 4 * (lane & 15);
+            const uint32_t cw = cl < nch ? cc[cl] : 0u;
+            uint32_t c4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) c4[i] = 4 * tid + i < nch ? cc[4 * tid + i] : 0u;
+            b1 = a.thr[2 * q];
+            above1 = a.thr[2 * q + 1];
+            uint32_t h4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) h4[i] = gh2[1023 - 4 * tid - i];
+            issue_q();
+            uint32_t run = block_excl_scan(c4[0] + c4[1] + c4[2] + c4[3], sh.scan, n_cand);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (4 * tid + i < nch) sh.pre[4 * tid + i] = run;
+                run += c4[i];
+            }
+            const bool long_chunk = nch > 4 * kU || c4[0] > 128u || c4[1] > 128u || c4[2] > 128u || c4[3] > 128u;
+            const bool any_long = __syncthreads_or(long_chunk) != 0;   // also publishes pre
+            b2 = bucket_from_regs<4>(h4, keep - above1, sh.scan, sh.res, above2);
+            in_lds = n_cand <= (uint32_t)kAsCap;
+            if (in_lds) {
+                // chunk offsets into scalar registers, then the wave's slots
+                // stored to their row-ordered places
+                const uint32_t pv = cl < nch ? sh.pre[cl] : 0u;
+#pragma unroll
+                for (int u = 0; u < kU; u++) {
+                    if (w + 4 * u >= nch) break;
+                    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)pv, u);
+                    const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cw, u);
+                    if (n > (uint32_t)a.cand_cap) continue;       // compacted again below
+                    const uint32_t j = 2 * lane;
+                    if (j < n) sh.kr[b + j] = (uint64_t)sv[u][0] | ((uint64_t)sv[u][1] << 32);
+                    if (j + 1 < n) sh.kr[b + j + 1] = (uint64_t)sv[u][2] | ((uint64_t)sv[u][3] << 32);
+                }
+                if (any_long) {
+                    // slots past the first 128 of a chunk, and chunks beyond
+                    // the first 64; chunks whose slots overflowed are
+                    // compacted again from the scores
+                    for (int c = w; c < nch; c += 4) {
+                        const uint32_t b = sh.pre[c], n = (c + 1 < nch ? sh.pre[c + 1] : n_cand) - b;
+                        if (n > (uint32_t)a.cand_cap) continue;
+                        for (uint32_t j = (c < 4 * kU ? 128u : 0u) + lane; j < n; j += 64)
+                            sh.kr[b + j] = cq[(size_t)c * a.cand_cap + j];
+                    }
+                    for (int c = 0; c < nch; c++) {
+                        const uint32_t b = sh.pre[c], e = c + 1 < nch ? sh.pre[c + 1] : n_cand;
+                        if (e - b <= (uint32_t)a.cand_cap) continue;
+                        const int64_t r0 = (int64_t)c * a.chunk;
+                        const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+                        as_compact(s, vec, r0, r1, b1, b, e, sh);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t pre2 = (b1 << 10) | b2;
+        const uint32_t need3 = keep - above1 - above2;
+        // third digit: the candidates of bucket (b1, b2), eight reads in
+        // flight per thread
+        if (in_lds) {
+            for (uint32_t i0 = 0; i0 < n_cand; i0 += 256 * 8) {
+                uint32_t k[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const uint32_t i = i0 + tid + 256 * u;
+                    k[u] = i < n_cand ? (uint32_t)(sh.kr[i] >> 32) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const uint32_t i = i0 + tid + 256 * u;
+                    if (i < n_cand && (k[u] >> 10) == pre2) atomicAdd(&sh.h3[k[u] & 1023], 1u);
+                }
+            }
+        } else {
+            as_hist_pass(s, vec, rows, 10, pre2, 0, 1024, sh.h3);
+        }
+        __syncthreads();
+        uint32_t above3;
+        const uint32_t b3 = find_bucket<1024>(sh.h3, need3, sh.scan, sh.res, above3);
+        const uint32_t thr = (pre2 << 10) | b3;
+        const uint32_t m_eq = need3 - above3;         // rows equal to thr kept, lowest rows first
+        const bool cut_ties = m_eq < sh.h3[b3];       // some rows equal to thr are dropped
+
+        if (in_lds) {
+            // thread t ranks candidates [per t, per (t + 1)), in row order
+            // (per a multiple of 2 and <= 48: its kept ones fit a 64-bit
+            // mask, read two at a time); its kept rows take positions
+            // [p0, p0 + popcount) of the selection
+            const uint32_t per = ((n_cand + 255) / 256 + 1) & ~1u;
+            const uint32_t i0 = per * tid, i1 = i0 + per < n_cand ? i0 + per : n_cand;
+            uint32_t tot, r = 0;
+            if (cut_ties) {
+                uint32_t n_eq = 0;
+                for (uint32_t i = i0; i < i1; i++) n_eq += (uint32_t)(sh.kr[i] >> 32) == thr ? 1u : 0u;
+                r = block_excl_scan(n_eq, sh.scan, tot);
+            }
+            uint64_t take = 0;
+            for (uint32_t i = i0; i < i1; i += 2) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t k = x[2 * h + 1];
+                    const bool in = i + h < i1;
+                    const bool eq = in && k == thr;
+                    const bool t = in && (k > thr || (eq && (!cut_ties || r < m_eq)));
+                    take |= (uint64_t)(t ? 1u : 0u) << (i + h - i0);
+                    r += eq ? 1u : 0u;
+                }
+            }
+            const uint32_t n_take = (uint32_t)__builtin_popcountll(take);
+            uint32_t p = block_excl_scan(n_take, sh.scan, tot);
+            // only the threads whose kept rows fall in this split emit;
+            // their candidates are read again two at a time, the reads
+            // independent of each other
+            if ((int64_t)(p + n_take) * kp > start && (int64_t)p * kp < split_end) {
+#pragma unroll 4
+                for (uint32_t i = i0; i < i1; i += 2) {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
+                    const uint32_t t2 = (uint32_t)(take >> (i - i0)) & 3u;
+                    if (t2 & 1u) emit(p++, (int32_t)x[0]);
+                    if (t2 & 2u) emit(p++, (int32_t)x[2]);
+                }
+            }
+        } else {
+            uint32_t eq_done = 0, out_done = 0;
+            for (int64_t sb = 0; sb < rows; sb += kAsTile) {
+                const int64_t rb = sb + kAsPer * tid;
+                float v[kAsPer];
+                load_scores<kAsPer>(s, rb, rows, vec, v);
+                uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+                for (int i = 0; i < kAsPer; i++) {
+                    const uint32_t k = order_key(v[i]);
+                    if (rb + i < rows) {
+                        gtm |= (k > thr ? 1u : 0u) << i;
+                        eqm |= (k == thr ? 1u : 0u) << i;
+                    }
+                }
+                uint32_t tot;
+                uint32_t r = eq_done + block_excl_scan(__builtin_popcount(eqm), sh.scan, tot);
+                eq_done += tot;
+                uint32_t take = gtm;
+#pragma unroll
+                for (int i = 0; i < kAsPer; i++) {
+                    if ((eqm >> i) & 1) {
+                        if (r < m_eq) take |= 1u << i;
+                        r++;
+                    }
+                }
+                uint32_t p = out_done + block_excl_scan(__builtin_popcount(take), sh.scan, tot);
+                out_done += tot;
+#pragma unroll
+                for (int i = 0; i < kAsPer; i++)
+                    if ((take >> i) & 1) emit(p++, (int32_t)(rb + i));
+            }
+        }
+        pooled = a.keep * kp;
+        tail = qi.nvis - (int32_t)rows * kp;
+        count = pooled + tail;
+    } else if (qi.mode == 0) {
+        count = qi.nvis;
+    }
+    // positions not taken by kept pools: the unpooled tail, the dense
+    // selection, or padding
+    for (int32_t P = start + tid; P < split_end; P += 256) {
+        if (P < pooled) continue;
+        int32_t tok = -1;
+        if (qi.mode == 1)
+            tok = P - pooled < tail ? (int32_t)qi.rows * kp + (P - pooled) : -1;
+        else if (qi.mode == 0)
+            tok = P < count ? P : -1;
+        sidx[P - start] = tok;
+        if (write_sel && P < a.sel_ld) dst[P] = tok;
+    }
+    if (write_sel) {
+        if (sp == a.n_split - 1)
+            for (int32_t P = split_end + tid; P < a.sel_ld; P += 256) dst[P] = -1;
+        if (sp == 0 && tid == 0) a.sel_count[q] = count;
+    }
+    return count;
+}
+
+// grid (4 * pairs rounded up to 8), 256 threads, as k_attend_wv; SCAN: the
+// queries' rows fit the one-pass selection (no k_filter ran).
+template <int D, bool SCAN>
+__global__ __launch_bounds__(256) void k_attend_sel(Args a) {
+    using Cfg = WvCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Cfg::WAVE];
+    __shared__ int32_t sidx[kWvMaxRows];
+    __shared__ float smx[4][16], ssum[4][16];
+    const int pairs = a.n_q * a.n_split;
+    const int pairs8 = (pairs + 7) & ~7;
+    const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
+    if (pair >= pairs) return;
+    const int q = pair / a.n_split, sp = pair % a.n_split;
+    const QInfo qi = query_info(a, q);
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int head = 16 * hg + n;
+    bf16x8 qreg[Cfg::ND];
+    // the queries are requested once the selection's own first loads are
+    // on their way
+    const uint16_t *qp = a.q + ((size_t)q * kHeads + head) * D + 8 * g;
+    auto issue_q = [&qreg, qp] {
+#pragma unroll
+        for (int j = 0; j < Cfg::ND; j++) qreg[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * j));
+    };
+    if (!SCAN) {
+        // k_filter has read the query's first-digit histogram: this
+        // work-group clears its slice of it for the next call.  (The
+        // second-digit histogram that follows it is read here by every
+        // work-group of the query; the next call's scorer clears it.)
+        const int slices = 4 * a.n_split, slice = 4 * sp + hg;
+        const int per = (kHistBins + slices - 1) / slices;
+        uint32_t *gh = a.hist + (size_t)q * kHistStride;
+        for (int i = slice * per + threadIdx.x; i < (slice + 1) * per && i < kHistBins; i += 256) gh[i] = 0;
+    }
+    AsShared &sh = *reinterpret_cast<AsShared *>(lds);
+    const int32_t count = as_select<SCAN>(a, sh, sidx, q, qi, sp, a.sel_export && hg == 0, issue_q);
+    const bool invalid = qi.mode == 2;
+    const int32_t start = sp * a.split_rows;
+    const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
+    const int nst = (nrows + kWvRows - 1) / kWvRows;
+    const int nj = nst > w ? (nst - w + 3) / 4 : 0;
+    const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
+    __syncthreads();   // sidx complete, and the selection's LDS (the row buffers) no longer read
+    wv_rows<D>(a, lds, sidx, smx, ssum, qreg, C, q, sp, hg, w, nj, invalid);
 }
 
 // Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
@@ -2284,7 +2711,20 @@ hipError_t launch_select(const Args &a, hipStream_t st, hipEvent_t ev0, hipEvent
 // ev[3] (not recorded when there is no merge); ev may be NULL.
 hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev) {
     const hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    if (a.attn_hs == 2) {
+    if (a.attn_sel) {
+        const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
+        if (a.D == 576) {
+            if (a.select_scan)
+                DSA_LAUNCH(e0, e1, (k_attend_sel<576, true>), dim3(4 * pairs8), dim3(256), st, a);
+            else
+                DSA_LAUNCH(e0, e1, (k_attend_sel<576, false>), dim3(4 * pairs8), dim3(256), st, a);
+        } else {
+            if (a.select_scan)
+                DSA_LAUNCH(e0, e1, (k_attend_sel<512, true>), dim3(4 * pairs8), dim3(256), st, a);
+            else
+                DSA_LAUNCH(e0, e1, (k_attend_sel<512, false>), dim3(4 * pairs8), dim3(256), st, a);
+        }
+    } else if (a.attn_hs == 2) {
         const unsigned pairs8 = (unsigned)((a.n_q * a.n_split + 7) & ~7);
         if (a.D == 576)
             DSA_LAUNCH(e0, e1, k_attend_wv<576>, dim3(4 * pairs8), dim3(256), st, a);

@@ -13,6 +13,8 @@ constexpr int kLatent = 512;      // latent / V / output width
 constexpr int kIdxHeads = 32;     // indexer heads
 constexpr int kIdxDim = 128;      // indexer head width
 constexpr int kHistBins = 4096;   // first radix digit: order-key bits 31..20
+constexpr int kHistH2 = kHistBins;               // the second-digit bins of the threshold bucket follow
+constexpr int kHistStride = kHistH2 + 1024;      // words per query
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxChunks = 1024;  // top-k chunks per query (one per k_select thread)
 constexpr int kAttnRows = 32;     // latent rows per attention step (one MFMA K block)
@@ -36,6 +38,7 @@ struct Plan {
     int32_t split_rows;           // selected rows per attention work-group
     int32_t n_split;              // attention splits per query
     int32_t attn_hs;              // attention kernel: 0 k_attend, 1 k_attend_hs, 2 k_attend_wv
+    int32_t attn_sel;             // fused decode step: top-k inside the attention (k_attend_sel)
     int32_t select_scan;          // 1: top-k in one kernel that scans the scores
     int32_t score_tile;           // key rows per score work-group
 
@@ -48,10 +51,11 @@ struct Plan {
     size_t hist_region;           // bytes of the histogram region (0 until placed)
 };
 
-constexpr size_t kHistQueryBytes = (size_t)kHistBins * 4;   // one query's first-digit histogram
+constexpr size_t kHistQueryBytes = (size_t)kHistStride * 4;   // one query's histograms
 
 // The histogram region of a workspace of ws_bytes: its first sixteenth,
-// rounded down to whole 16 KiB histograms.  It depends on the workspace
+// rounded down to whole blocks of kHistStride words (a query's first-digit
+// histogram and the second-digit histogram of its threshold bucket).  It depends on the workspace
 // size only, never on the call's shape, so calls of different query counts
 // and context lengths on one workspace all find their histograms inside
 // the same region -- which only histogram accumulation (and the clearing
@@ -100,6 +104,21 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     // kernel, DSA_ATTN_PAIRS the (query, split) target.
     p.attn_hs = n_q < 4 ? 1 : n_q <= 64 ? 2 : 0;
     if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) == 2 ? 2 : atoi(e) ? 1 : 0;
+    // The fused decode step of up to 64 queries (not a prefill chunk) runs
+    // its top-k inside the wave-private attention, k_attend_sel: no
+    // k_select launch and no selection round trip through memory.
+    // DSA_ATTN_SEL=0 keeps k_select + the attention kernel above instead.
+    p.attn_sel = n_q <= 64 ? 1 : 0;
+    if (const char *e = getenv("DSA_ATTN_SEL")) p.attn_sel = p.attn_sel && atoi(e) != 0;
+    // k_attend_sel takes the candidates of up to 64 chunks per query straight
+    // into registers (16 chunks per wave): larger chunks when a query has more
+    if (p.attn_sel) {
+        int64_t ch2 = p.chunk;
+        while ((p.max_rows + ch2 - 1) / ch2 > 64) ch2 <<= 1;
+        p.chunk = (int32_t)ch2;
+        p.n_chunks = (int32_t)((p.max_rows + ch2 - 1) / ch2);
+        p.cand_cap = p.chunk / 4;
+    }
     // k_attend runs one work-group per CU (143 KiB of LDS): as many splits as
     // keep the grid within one round of 256 work-groups (8 x 128K at 128
     // queries: 2 splits, 100 us for attention + merge against 144 us with 1)
@@ -113,7 +132,7 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     sr = (sr + 31) / 32 * 32;
     if (sr < 64) sr = 64;
     if (sr > kMaxSplitRows) sr = kMaxSplitRows;
-    if (p.attn_hs == 2 && sr > kWvMaxRows) sr = kWvMaxRows;
+    if ((p.attn_hs == 2 || p.attn_sel) && sr > kWvMaxRows) sr = kWvMaxRows;
     p.split_rows = (int32_t)sr;
     p.n_split = (int32_t)((p.sel_max + sr - 1) / sr);
 
@@ -150,9 +169,9 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     return p;
 }
 
-// Smallest workspace for the plan: with k = the histograms its first
-// sixteenth holds (k = ws / 256 KiB, rounded down), k >= n_q and
-// k * 16 KiB + body <= ws.  Growing ws for the body can raise k, which the
+// Smallest workspace for the plan: with k = the histogram blocks its first
+// sixteenth holds (k = ws / (16 blocks), rounded down), k >= n_q and
+// k blocks + body <= ws.  Growing ws for the body can raise k, which the
 // loop follows until both hold.
 inline size_t workspace_bytes(const Plan &p) {
     size_t k = (size_t)p.n_q;

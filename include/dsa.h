@@ -30,10 +30,13 @@
  *    work it enqueued has finished, and allocates no device memory.
  *  - Workspace contract: a workspace must be zero-filled once before its
  *    first use (dsa_workspace_init, or any zero fill).  Its first sixteenth
- *    (rounded down to whole 16 KiB blocks) holds the per-query histograms
- *    of the top-k; each call accumulates into the first n_q blocks and
- *    clears them again before its work completes, and puts everything else
- *    after that region.  So one workspace serves any sequence of calls,
+ *    (rounded down to whole 20 KiB blocks) holds per-query histograms of the
+ *    top-k, block q for the call's query q: the 16 KiB first-digit
+ *    histogram, which each call accumulates and clears again before its
+ *    work completes, so that it is zero between calls, then a 4 KiB
+ *    second-digit histogram, which each call clears before it uses it.
+ *    Everything else follows that region.  So one workspace serves any
+ *    sequence of calls,
  *    with any query counts and visible bounds, with no clearing in between
  *    (a serving loop whose batch size changes step to step keeps one
  *    workspace), provided that
@@ -124,9 +127,9 @@ typedef struct {
 
 /* Bytes of workspace that dsa_topk, dsa_mla_attend and dsa_decode_step need
  * for this geometry, query count and visible bound (the maximum of the three;
- * one workspace serves all of them): at least 16 x n_q x 16 KiB, so that the
- * histogram region (the first sixteenth) holds n_q histograms, and large
- * enough that the rest fits after that region.  Returns 0 for an unsupported geometry
+ * one workspace serves all of them): at least 16 x n_q x 20 KiB, so that the
+ * histogram region (the first sixteenth) holds n_q blocks, and large enough
+ * that the rest fits after that region.  Returns 0 for an unsupported geometry
  * or sizes out of range (n_q outside 1..65535, max_nvis outside 1..2^31 - 1). */
 size_t dsa_workspace_bytes(const dsa_geometry *geom, int32_t n_q, int64_t max_nvis);
 

@@ -57,3 +57,21 @@ def check_attention(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
 
 def gpu_arch() -> str:
     return torch.cuda.get_device_properties(0).gcnArchName
+
+
+HIST_BLOCK = 20480   # bytes per query in the workspace's histogram region
+HIST_FIRST = 16384   # of which the first-digit histogram, zero between calls
+
+
+def hist_region(ws_bytes: int) -> int:
+    """Bytes of a workspace's histogram region: its first sixteenth, in whole
+    per-query blocks."""
+    return (ws_bytes // 16) // HIST_BLOCK * HIST_BLOCK
+
+
+def first_digit_dirty(ws) -> int:
+    """Non-zero bytes in the first-digit histograms of every block of the
+    workspace's histogram region (which must be zero between calls)."""
+    H = hist_region(ws.numel())
+    blocks = ws[:H].view(-1, HIST_BLOCK)[:, :HIST_FIRST]
+    return int(blocks.count_nonzero())

@@ -87,6 +87,7 @@ def test_stream_read_probe():
 
 # name, geometry, n_seq, T, q_seq, q_nvis, whether the filter kernel runs
 # (rows > 16,384), whether the merge runs (more than one split)
+# name, geometry, n_seq, T, q_seq, q_nvis, filter runs, k_reduce runs
 TIMED = [
     ("tok_chunked", dict(I.GEOM_TOKEN), 4, 40000, [0, 1, 2, 3, 0], [40000, 30001, 20480, 1500, 0], True, True),
     ("one_query_scan", dict(I.GEOM_TOKEN), 1, 9000, [0], [9000], False, True),
@@ -96,7 +97,8 @@ TIMED = [
 @pytest.mark.parametrize("case", TIMED, ids=[c[0] for c in TIMED])
 def test_timing_events_time_the_kernels_that_ran(case):
     """With timing events set, the step gives the same outputs, reports the
-    kernels it ran (the filter only for the chunked top-k), and each of them
+    kernels it ran (the filter only for the chunked top-k, no separate select
+    kernel for a decode batch), and each of them
     has a positive start-to-stop interval inside the call's own bracket."""
     name, g, n_seq, T, q_seq, q_nvis, filt, merge = case
     log(f"timing events {name}")
@@ -118,7 +120,9 @@ def test_timing_events_time_the_kernels_that_ran(case):
     evs[11].record()
     torch.cuda.synchronize()
     ran = B.timing_ran()
-    assert ran & 0b01101 == 0b01101, f"score, select and attend always run: {ran:#b}"
+    # decode batches of up to 64 queries select inside the attention kernel
+    assert ran & 0b01001 == 0b01001, f"score and attend always run: {ran:#b}"
+    assert not ran & 0b00100, f"no separate select kernel for a decode batch: {ran:#b}"
     assert bool(ran & 0b00010) == filt and bool(ran & 0b10000) == merge, f"{ran:#b}"
     whole = evs[10].elapsed_time(evs[11])
     for j in range(5):

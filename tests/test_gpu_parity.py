@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import check_attention, check_selection, log, oracle_decode, gpu_arch
+from gpu_common import (HIST_BLOCK, check_attention, check_selection, first_digit_dirty, gpu_arch,
+                        hist_region, log, oracle_decode)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -74,10 +75,18 @@ def test_scores_bit_exact(case):
         assert np.isnan(got[j, rows:]).all(), f"{name} q{j} wrote past rows"
 
 
+# fused-step paths for a decode batch: the top-k inside the attention kernel
+# (default), or k_select + the attention kernel
+PATHS = {"fused": {}, "select": {"DSA_ATTN_SEL": "0"}}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("case", list(enumerate(CASES)), ids=[c[0] for c in CASES])
-def test_decode_step_matches_oracle(case):
+def test_decode_step_matches_oracle(case, path, monkeypatch):
+    for k, v in PATHS[path].items():
+        monkeypatch.setenv(k, v)
     i, (name, g, n_seq, T, q_seq, q_nvis, kr) = case
-    log(f"decode {name}")
+    log(f"decode {name} ({path})")
     w = make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr)
     dw = DeviceWorkload(w)
     dw.sel.fill_(-7)
@@ -86,11 +95,11 @@ def test_decode_step_matches_oracle(case):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy(), sel, cnt, name)
     check_attention(dw.out.cpu().numpy(), dw.lse.cpu().numpy(), out, lse, name)
-    # the histogram region (the workspace's first sixteenth, in whole 16 KiB
-    # histograms) is all zero again after the call (workspace contract)
-    hist_bytes = (dw.ws.numel() // 16) // 16384 * 16384
-    assert hist_bytes >= w.n_q * 16384
-    assert int(dw.ws[:hist_bytes].count_nonzero()) == 0, f"{name}: histogram left dirty"
+    # the first-digit histograms of the histogram region (the workspace's
+    # first sixteenth, in whole per-query blocks) are all zero again after
+    # the call (workspace contract)
+    assert hist_region(dw.ws.numel()) >= w.n_q * HIST_BLOCK
+    assert first_digit_dirty(dw.ws) == 0, f"{name}: histogram left dirty"
     # a second call on the same workspace gives the same result bit for bit
     out1, sel1 = dw.out.clone(), dw.sel.clone()
     dw.decode_step()

@@ -3,15 +3,15 @@ visible bound change from call to call, with no clearing in between: a
 serving loop whose batch changes step to step (TensorSharp2 GLM docs,
 "Serving concurrent requests": a batched decode over the concurrent
 sequences, one sequence at a time when batching declines).  Every call is
-compared with the oracle, and the workspace's histogram region must be all
-zero after each call."""
+compared with the oracle, and the first-digit histograms of the workspace's
+histogram region must be all zero after each call."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import check_attention, check_selection, log
+from gpu_common import HIST_BLOCK, check_attention, check_selection, first_digit_dirty, hist_region, log
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -34,10 +34,6 @@ CALLS = [
 ]
 
 
-def hist_region(ws_bytes: int) -> int:
-    return (ws_bytes // 16) // 16384 * 16384
-
-
 def test_workspace_reused_across_batch_shapes():
     w = I.decode_128k(8)
     g = w.geom
@@ -45,8 +41,7 @@ def test_workspace_reused_across_batch_shapes():
     cache = torch.from_numpy(w.cache).to(dev)
     idx_k = torch.from_numpy(w.idx_k).to(dev)
     ws = B.new_workspace(g, 8, T, device=dev)
-    H = hist_region(ws.numel())
-    assert H >= 8 * 16384
+    assert hist_region(ws.numel()) >= 8 * HIST_BLOCK
     sel_ld = g["top_k"] + g["kpool"] - 1
     for k, (seqs, nvis) in enumerate(CALLS):
         n_q = len(seqs)
@@ -66,7 +61,7 @@ def test_workspace_reused_across_batch_shapes():
         b = B.batch(q_seq, q_nvis, int(nv.max()), 8)
         B.decode_step(g, b, iq, iw, idx_k, w.key_rows, q, cache, T, sel, sel_ld, cnt, out, lse, ws)
         torch.cuda.synchronize()
-        assert int(ws[:H].count_nonzero()) == 0, f"call {k}: histogram region left dirty"
+        assert first_digit_dirty(ws) == 0, f"call {k}: histogram region left dirty"
         rsel, rcnt, rout, rlse = O.decode_step(g, qs, nv, w.idx_q[qs], w.idx_w[qs], w.idx_k, w.q[qs], w.cache)
         check_selection(sel.cpu().numpy(), cnt.cpu().numpy(), rsel, rcnt, f"call {k}")
         check_attention(out.cpu().numpy(), lse.cpu().numpy(), rout, rlse, f"call {k}")
