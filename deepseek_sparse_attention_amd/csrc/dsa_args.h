@@ -46,6 +46,7 @@ struct Args {
     int32_t attn_sel;     // fused step: the top-k runs inside the attention (k_attend_sel)
     int32_t hist_on;      // the scorer accumulates the first-digit histograms
     int32_t sel_export;   // k_attend_sel writes the selection and its count to sel / sel_count
+    int32_t score_valu;   // decode scorer on the vector ALU (k_score_valu), for measurement
 };
 
 // Arguments of the k-pool key producer.

@@ -395,6 +395,79 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     }
 }
 
+// The decode scorer on the vector ALU instead of MFMA, kept to measure the
+// two against each other (DSA_SCORE_VALU=1): one key row per lane, its 128
+// dimensions widened to fp32 in registers, the query's 32 heads of 128 in
+// fp32 broadcast from LDS, one v_fma_f32 per product (exact here, as on
+// MFMA: the products and their sums are integers below 2^24), then the same
+// ReLU, weights, scores and first-digit histogram as k_score.  (The bf16
+// pair dot product v_dot2_f32_bf16 does not keep such sums exact.)  bf16
+// indexer inputs, decode batches only.  grid (tiles of 256 rows, n_q), 256
+// threads.
+__global__ __launch_bounds__(256) void k_score_valu(Args a) {
+    __shared__ __attribute__((aligned(16))) f32x4 qs[kIdxHeads * kIdxDim / 4];
+    __shared__ float wsh[kIdxHeads];
+    __shared__ uint32_t lhist[kHistBins];
+    const int q = blockIdx.y;
+    const QInfo qi = query_info(a, q);
+    if (qi.mode == 2 || (a.fused && qi.mode == 0)) return;
+    const int64_t rows = qi.rows;
+    if ((int64_t)blockIdx.x * 256 >= rows) return;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool hist = a.hist_on != 0;
+    const uint32_t *qg = reinterpret_cast<const uint32_t *>(a.idx_q + (size_t)q * kIdxHeads * kIdxDim);
+    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 4; i += 256) {
+        const uint32_t x0 = qg[2 * i], x1 = qg[2 * i + 1];   // bf16 pairs -> fp32 (exact)
+        qs[i] = f32x4{__uint_as_float(x0 << 16), __uint_as_float(x0 & 0xFFFF0000u), __uint_as_float(x1 << 16),
+                      __uint_as_float(x1 & 0xFFFF0000u)};
+    }
+    if (threadIdx.x < kIdxHeads) wsh[threadIdx.x] = a.idx_w[(size_t)q * kIdxHeads + threadIdx.x];
+    if (hist)
+        for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+    if (a.attn_sel && !a.select_scan && blockIdx.x == 0) {
+        uint32_t *h2 = a.hist + (size_t)q * kHistStride + kHistH2;
+        for (int i = threadIdx.x; i < 1024; i += 256) h2[i] = 0;
+    }
+    u32x4 kv[16];
+    const int64_t rr = r < rows ? r : rows - 1;
+    const u32x4 *kg = reinterpret_cast<const u32x4 *>(a.idx_k + ((size_t)qi.seq * a.key_stride + rr) * kIdxDim);
+#pragma unroll
+    for (int j = 0; j < 16; j++) kv[j] = kg[j];
+    float kf[kIdxDim];
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            kf[8 * j + 2 * e] = __uint_as_float(kv[j][e] << 16);
+            kf[8 * j + 2 * e + 1] = __uint_as_float(kv[j][e] & 0xFFFF0000u);
+        }
+    __syncthreads();
+    float score = 0.f;
+#pragma unroll 1
+    for (int h = 0; h < kIdxHeads; h++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kIdxDim / 4; j++) {
+            const f32x4 qv = qs[h * (kIdxDim / 4) + j];
+            acc = __builtin_fmaf(kf[4 * j], qv[0], acc);
+            acc = __builtin_fmaf(kf[4 * j + 1], qv[1], acc);
+            acc = __builtin_fmaf(kf[4 * j + 2], qv[2], acc);
+            acc = __builtin_fmaf(kf[4 * j + 3], qv[3], acc);
+        }
+        score += wsh[h] * relu(acc);
+    }
+    if (r < rows) {
+        a.scores[(size_t)q * a.score_ld + r] = score;
+        if (hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
+    }
+    if (hist) {
+        __syncthreads();
+        uint32_t *gh = a.hist + (size_t)q * kHistStride;
+        for (int i = threadIdx.x; i < kHistBins; i += 256)
+            if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
+    }
+}
+
 // Chunked-prefill / verify-window indexer: a dense [queries x 32 heads] x
 // [128 x keys] contraction per work-group.  grid (key ranges, blocks), 1024
 // threads = 16 waves (4 per SIMD: the LDS of one work-group fills the CU, so
@@ -2672,6 +2745,8 @@ hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st, hip
     // sequence: one work-group per query, striding over the tiles
     if (a.prefill)
         DSA_LAUNCH(nullptr, ev1, (k_score<true, F16>), dim3(1, a.n_q), dim3(256), st, a);
+    else if (!F16 && a.score_valu)
+        DSA_LAUNCH(ev0, ev1, k_score_valu, dim3((unsigned)((max_rows + 255) / 256), a.n_q), dim3(256), st, a);
     else
         DSA_LAUNCH(ev0, ev1, (k_score<false, F16>),
                    dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(256), st, a);

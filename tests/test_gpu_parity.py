@@ -56,10 +56,15 @@ def make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr):
     return I.make_workload(name, 100 + i, g, n_seq, T, q_seq, q_nvis, key_range=kr)
 
 
+@pytest.mark.parametrize("scorer", ["mfma", "valu"])
 @pytest.mark.parametrize("case", list(enumerate(CASES)), ids=[c[0] for c in CASES])
-def test_scores_bit_exact(case):
+def test_scores_bit_exact(case, scorer, monkeypatch):
+    """Scores of the MFMA scorer and of its vector-ALU variant (kept to
+    measure the two against each other), bit for bit."""
+    if scorer == "valu":
+        monkeypatch.setenv("DSA_SCORE_VALU", "1")
     i, (name, g, n_seq, T, q_seq, q_nvis, kr) = case
-    log(f"scores {name}")
+    log(f"scores {name} ({scorer})")
     w = make_case(i, name, g, n_seq, T, q_seq, q_nvis, kr)
     dw = DeviceWorkload(w)
     rows_max = dw.max_nvis // g["kpool"]
