@@ -2083,20 +2083,21 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int kp = a.kpool;
     const int32_t start = sp * a.split_rows, split_end = start + a.split_rows;
-    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
     int32_t count = 0;
     int32_t pooled = 0, tail = 0;   // sparse: positions [0, pooled) are kept pools, then `tail` tail tokens
     if (qi.mode != 1) issue_q();
     // kept row number p (ascending) -> token positions p kp .. p kp + kp - 1
+    // of this split (the exported selection is copied from sidx later)
     auto emit = [&](uint32_t p, int32_t r) {
+        if (kp == 1) {
+            const int32_t P = (int32_t)p;
+            if (P >= start && P < split_end) sidx[P - start] = r;
+            return;
+        }
 #pragma unroll 1
         for (int j = 0; j < kp; j++) {
             const int32_t P = (int32_t)p * kp + j;
-            if (P >= start && P < split_end) {
-                const int32_t tok = r * kp + j;
-                sidx[P - start] = tok;
-                if (write_sel && P < a.sel_ld) dst[P] = tok;
-            }
+            if (P >= start && P < split_end) sidx[P - start] = r * kp + j;
         }
     };
     if (qi.mode == 1) {
@@ -2268,17 +2269,19 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
                 }
             }
             const uint32_t n_take = (uint32_t)__builtin_popcountll(take);
-            uint32_t p = block_excl_scan(n_take, sh.scan, tot);
-            // only the threads whose kept rows fall in this split emit;
-            // their candidates are read again two at a time, the reads
-            // independent of each other
+            const uint32_t p = block_excl_scan(n_take, sh.scan, tot);
+            // only the threads whose kept rows fall in this split emit; a
+            // kept candidate's position is p plus the kept ones before it
+            // in the thread's mask, so the candidates are independent
             if ((int64_t)(p + n_take) * kp > start && (int64_t)p * kp < split_end) {
 #pragma unroll 4
                 for (uint32_t i = i0; i < i1; i += 2) {
                     const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
-                    const uint32_t t2 = (uint32_t)(take >> (i - i0)) & 3u;
-                    if (t2 & 1u) emit(p++, (int32_t)x[0]);
-                    if (t2 & 2u) emit(p++, (int32_t)x[2]);
+                    const uint32_t b = i - i0;
+                    const uint32_t t2 = (uint32_t)(take >> b) & 3u;
+                    const uint32_t pb = p + (uint32_t)__builtin_popcountll(take & ((1ull << b) - 1ull));
+                    if (t2 & 1u) emit(pb, (int32_t)x[0]);
+                    if (t2 & 2u) emit(pb + (t2 & 1u), (int32_t)x[2]);
                 }
             }
         } else {
@@ -2330,14 +2333,21 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
         else if (qi.mode == 0)
             tok = P < count ? P : -1;
         sidx[P - start] = tok;
-        if (write_sel && P < a.sel_ld) dst[P] = tok;
     }
-    if (write_sel) {
-        if (sp == a.n_split - 1)
-            for (int32_t P = split_end + tid; P < a.sel_ld; P += 256) dst[P] = -1;
-        if (sp == 0 && tid == 0) a.sel_count[q] = count;
-    }
+    if (write_sel && sp == 0 && tid == 0) a.sel_count[q] = count;
     return count;
+}
+
+// The split's part of the exported selection, copied from sidx once it is
+// complete (coalesced, every thread), then the padding after the last split.
+__device__ __forceinline__ void as_export(const Args &a, const int32_t *sidx, int q, int sp) {
+    int32_t *dst = a.sel + (size_t)q * a.sel_ld;
+    const int32_t start = sp * a.split_rows;
+    int32_t end = start + a.split_rows;
+    end = end < a.sel_ld ? end : a.sel_ld;
+    for (int32_t P = start + (int32_t)threadIdx.x; P < end; P += 256) dst[P] = sidx[P - start];
+    if (sp == a.n_split - 1)
+        for (int32_t P = start + a.split_rows + (int32_t)threadIdx.x; P < a.sel_ld; P += 256) dst[P] = -1;
 }
 
 // grid (4 * pairs rounded up to 8), 256 threads, as k_attend_wv; SCAN: the
@@ -2384,6 +2394,7 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
     const int nj = nst > w ? (nst - w + 3) / 4 : 0;
     const uint8_t *C = reinterpret_cast<const uint8_t *>(a.cache + (size_t)(invalid ? 0 : qi.seq) * a.cache_stride * D);
     __syncthreads();   // sidx complete, and the selection's LDS (the row buffers) no longer read
+    if (a.sel_export && hg == 0) as_export(a, sidx, q, sp);
     wv_rows<D>(a, lds, sidx, smx, ssum, qreg, C, q, sp, hg, w, nj, invalid);
 }
 
