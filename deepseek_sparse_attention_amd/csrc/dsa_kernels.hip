@@ -162,6 +162,12 @@ __device__ uint32_t bucket_from_regs(const uint32_t (&c)[PER], uint32_t need, ui
         res[0] = bin;
         res[1] = run_at;
     }
+    // fewer than `need` items in all (a histogram that does not match the
+    // scores): bin 0, with every item above it counted
+    if (threadIdx.x == 255 && before + s < need) {
+        res[0] = 0;
+        res[1] = before + s - c[PER - 1];
+    }
     __syncthreads();
     above = res[1];
     const uint32_t b = res[0];
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     const bool early = !STRIDE && a.q_seq == nullptr && rmax >= 1;
     if (early) {
         const uint8_t *K0 = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)q * a.key_stride * kIdxDim);
-        const int64_t b0 = (int64_t)blockIdx.x * a.score_tile + 64 * w;
+        const int64_t b0 = (a.score_ilv ? 256 * (int64_t)blockIdx.x : (int64_t)blockIdx.x * a.score_tile) + 64 * w;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             int64_t r = b0 + 4 * i + (lane >> 4);
@@ -292,7 +298,8 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
         return;
     }
     const int64_t rows = qi.rows;
-    if ((int64_t)blockIdx.x * a.score_tile >= rows) {
+    const bool ilv = !STRIDE && a.score_ilv;
+    if ((int64_t)blockIdx.x * (ilv ? 256 : a.score_tile) >= rows) {
         drain();
         return;
     }
@@ -326,32 +333,23 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     float *srow = a.scores + (size_t)q * a.score_ld;
     const int st_mine = 2 * (g & 1) + (g >> 1);
     uint8_t *tb = tiles[w];
-    auto fetch = [&](int64_t base) {
+    auto fetch = [&](u32x4 (&vv)[16], int64_t base) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             int64_t r = base + 4 * i + (lane >> 4);
             r = r < rows ? r : rows - 1;
-            v[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (lane & 15)));
+            vv[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (lane & 15)));
         }
     };
-    // tiles t0 = blockIdx.x * tile, stepping by the grid (one pass in the
-    // common case; the prefill fix-up grid has one work-group per query)
-    for (int64_t t0 = (int64_t)blockIdx.x * a.score_tile; t0 < rows;
-         t0 = STRIDE ? t0 + (int64_t)gridDim.x * a.score_tile : rows) {
-    const int64_t end = t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
-    int64_t base = t0 + 64 * w;
-    if (early) {
-        if (base >= end) drain();              // no step for this wave in a short last tile
-    } else if (base < end) {
-        fetch(base);
-    }
-    for (; base < end; base += 256) {
+    // one 64-row step from the registers vv: staged in the LDS tile, vv
+    // refilled with the wave's next step (row `ahead`), then scored
+    auto step = [&](u32x4 (&vv)[16], int64_t base, int64_t ahead, int64_t end) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int r = 4 * i + (lane >> 4), pc = lane & 15;
-            *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 15))) = v[i];
+            *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 15))) = vv[i];
         }
-        if (base + 256 < end) fetch(base + 256);
+        if (ahead < end) fetch(vv, ahead);
         __builtin_amdgcn_wave_barrier();
         float p[4];
 #pragma unroll
@@ -385,7 +383,20 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             srow[row] = score;
             if (hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
         }
+    };
+    // tiles t0 = blockIdx.x * tile, stepping by the grid (one pass in the
+    // common case; the prefill fix-up grid has one work-group per query)
+    const int64_t wstep = ilv ? 256 * (int64_t)gridDim.x : 256;
+    for (int64_t t0 = (int64_t)blockIdx.x * (ilv ? 256 : a.score_tile); t0 < rows;
+         t0 = STRIDE ? t0 + (int64_t)gridDim.x * a.score_tile : rows) {
+    const int64_t end = !ilv && t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
+    int64_t base = t0 + 64 * w;
+    if (early) {
+        if (base >= end) drain();              // no step for this wave in a short last tile
+    } else if (base < end) {
+        fetch(v, base);
     }
+    for (; base < end; base += wstep) step(v, base, base + wstep, end);
     }
     if (hist) {
         __syncthreads();
@@ -834,6 +845,11 @@ __device__ uint32_t sel_find(const uint32_t (&c)[PER], uint32_t need, uint32_t *
         res[0] = bin;
         res[1] = run_at;
         res[2] = cnt;
+    }
+    if (threadIdx.x == kSelThreads - 1 && before + s < need) {   // as bucket_from_regs
+        res[0] = 0;
+        res[1] = before + s - c[PER - 1];
+        res[2] = c[PER - 1];
     }
     __syncthreads();
     above = res[1];
@@ -1745,11 +1761,10 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
     const uint32_t voff = 16 * lane;
     const uint32_t wb_lds = __builtin_amdgcn_readfirstlane(lds_addr(wb));
     const uint64_t c_base = reinterpret_cast<uint64_t>(C), z_base = reinterpret_cast<uint64_t>(kZeroRow);
-    // address of row t, or of the zero row for t < 0, without a branch
-    auto row_addr = [&](int32_t t) -> uint64_t {
-        const uint64_t m = (uint64_t)(int64_t)(t >> 31);
-        return ((c_base + (uint64_t)(uint32_t)t * (2 * D)) & ~m) | (z_base & m);
-    };
+    // address of row t, or of the zero row for t outside [0, cache_stride)
+    const int64_t cstride = a.cache_stride;
+    auto row_ok = [cstride](int32_t t) { return t >= 0 && (int64_t)t < cstride; };
+    auto row_addr = [&](int32_t t) -> uint64_t { return row_ok(t) ? c_base + (uint64_t)(uint32_t)t * (2 * D) : z_base; };
     // lane & 15 holds the index of row lane & 15 of the wave's step j
     auto idx_v = [&](int j) -> int32_t { return j < nj ? sidx[kWvRows * (w + 4 * j) + (lane & 15)] : -1; };
     auto issue = [&](int j, int32_t iv, int b) {
@@ -1796,7 +1811,7 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
             else
                 wait_vm<0>();
             const uint8_t *vb = wb + (j & 1) * Cfg::BUF;
-            const uint64_t okmask = __ballot(lane < kWvRows && iv >= 0);
+            const uint64_t okmask = __ballot(lane < kWvRows && row_ok(iv));
 
             // S^T of the step's 16 rows (lane: rows 4g .. 4g + 3 of head n),
             // two independent accumulation chains
@@ -2385,6 +2400,9 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
         uint32_t *gh = a.hist + (size_t)q * kHistStride;
         for (int i = slice * per + threadIdx.x; i < (slice + 1) * per && i < kHistBins; i += 256) gh[i] = 0;
     }
+    // a position the selection leaves unset (only possible where the
+    // workspace's histograms do not match the scores) reads as no row
+    for (int r = threadIdx.x; r < a.split_rows; r += 256) sidx[r] = -1;
     AsShared &sh = *reinterpret_cast<AsShared *>(lds);
     const int32_t count = as_select<SCAN>(a, sh, sidx, q, qi, sp, a.sel_export && hg == 0, issue_q);
     const bool invalid = qi.mode == 2;
