@@ -106,11 +106,15 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     // kernel, DSA_ATTN_PAIRS the (query, split) target.
     p.attn_hs = n_q < 4 ? 1 : n_q <= 64 ? 2 : 0;
     if (const char *e = getenv("DSA_ATTN_HS")) p.attn_hs = atoi(e) == 2 ? 2 : atoi(e) ? 1 : 0;
-    // The fused decode step of up to 64 queries (not a prefill chunk) runs
+    // The fused decode step of up to 8 queries (not a prefill chunk) runs
     // its top-k inside the wave-private attention, k_attend_sel: no
-    // k_select launch and no selection round trip through memory.
-    // DSA_ATTN_SEL=0 keeps k_select + the attention kernel above instead.
-    p.attn_sel = n_q <= 64 ? 1 : 0;
+    // k_select launch and no selection round trip through memory.  Every
+    // work-group repeats its query's selection, which beyond 8 queries
+    // costs more than the launch it saves (attention with top-k at 128K,
+    // us: 8 queries 24.0 fused vs 23.7 + a launch; 16: 36.3 vs 31.1; 64:
+    // 82.8 vs 71.7).  DSA_ATTN_SEL=0 keeps k_select + the attention kernel
+    // above instead.
+    p.attn_sel = n_q <= 8 ? 1 : 0;
     if (const char *e = getenv("DSA_ATTN_SEL")) p.attn_sel = p.attn_sel && atoi(e) != 0;
     // k_attend_sel takes the candidates of up to 64 chunks per query straight
     // into registers (16 chunks per wave): larger chunks when a query has more

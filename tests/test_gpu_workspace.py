@@ -83,3 +83,40 @@ def test_workspace_too_small_for_the_call_is_refused():
     assert e.value.status == B.DSA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
+
+
+@pytest.mark.parametrize("path", ["fused", "select"])
+@pytest.mark.parametrize("T", [40000, 9000])
+def test_garbage_workspace_is_survived_and_cleared(T, path, monkeypatch):
+    """A workspace whose every byte is random breaks the rule that its
+    first-digit histograms are zero between calls.  Where the top-k reads
+    them (the chunked top-k at T = 40,000; k_select at T = 9,000) the first
+    call's selection is meaningless, but every row it reads still lies in
+    the caches, so it completes, and it clears its queries' histograms, so
+    the next call of the same shape on that workspace is exact.  The fused
+    step's one-pass top-k (T = 9,000) reads no histogram from the workspace:
+    both of its calls are exact."""
+    monkeypatch.setenv("DSA_ATTN_SEL", "1" if path == "fused" else "0")
+    w = I.make_workload(f"ws_garbage_{T}", 91, I.GEOM_TOKEN, 2, T, np.arange(2), [T, T - 1234])
+    g = w.geom
+    dev = torch.device("cuda")
+    ws = B.new_workspace(g, 2, T, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(T + (path == "fused"))
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=dev, generator=gen))
+    t = {k: torch.from_numpy(getattr(w, k)).to(dev) for k in ("cache", "idx_k", "q", "idx_q", "idx_w")}
+    sel_ld = g["top_k"] + g["kpool"] - 1
+    b = B.batch(None, torch.from_numpy(w.q_nvis).to(dev), int(w.q_nvis.max()), 2)
+    rsel, rcnt, rout, rlse = O.decode_step(g, w.q_seq, w.q_nvis, w.idx_q, w.idx_w, w.idx_k, w.q, w.cache)
+    for k in range(2):
+        log(f"garbage workspace T={T} {path}: call {k}")
+        sel = torch.full((2, sel_ld), -7, dtype=torch.int32, device=dev)
+        cnt = torch.empty(2, dtype=torch.int32, device=dev)
+        out = torch.empty((2, g["n_heads"], g["d_latent"]), dtype=torch.float32, device=dev)
+        lse = torch.empty((2, g["n_heads"]), dtype=torch.float32, device=dev)
+        B.decode_step(g, b, t["idx_q"], t["idx_w"], t["idx_k"], w.key_rows, t["q"], t["cache"], w.T, sel, sel_ld,
+                      cnt, out, lse, ws)
+        torch.cuda.synchronize()
+        if k == 1 or (T <= 16384 and path == "fused"):
+            check_selection(sel.cpu().numpy(), cnt.cpu().numpy(), rsel, rcnt, f"T={T} {path}")
+            check_attention(out.cpu().numpy(), lse.cpu().numpy(), rout, rlse, f"T={T} {path}")
