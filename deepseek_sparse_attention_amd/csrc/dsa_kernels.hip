@@ -2050,6 +2050,8 @@ struct AsShared {
     uint32_t h3[1024];
     uint32_t scan[4];
     uint32_t res[4];
+    uint32_t epos[256];                  // emission: first position of each thread's kept rows
+    uint64_t etake[256];                 // and the mask of its kept candidates
 };
 static_assert(sizeof(AsShared) <= 4 * WvCfg<512>::WAVE, "the selection fits the row buffers");
 
@@ -2268,49 +2270,76 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
         const uint32_t b3 = find_bucket<1024>(sh.h3, need3, sh.scan, sh.res, above3);
         const uint32_t thr = (pre2 << 10) | b3;
         const uint32_t m_eq = need3 - above3;         // rows equal to thr kept, lowest rows first
-        const bool cut_ties = m_eq < sh.h3[b3];       // some rows equal to thr are dropped
 
         if (in_lds) {
             // thread t ranks candidates [per t, per (t + 1)), in row order
-            // (per a multiple of 2 and <= 48: its kept ones fit a 64-bit
-            // mask, read two at a time); its kept rows take positions
-            // [p0, p0 + popcount) of the selection
+            // (per a multiple of 2 and <= 48, so that its candidates above
+            // and at the threshold fit 64-bit masks; read two at a time)
             const uint32_t per = ((n_cand + 255) / 256 + 1) & ~1u;
             const uint32_t i0 = per * tid, i1 = i0 + per < n_cand ? i0 + per : n_cand;
-            uint32_t tot, r = 0;
-            if (cut_ties) {
-                uint32_t n_eq = 0;
-                for (uint32_t i = i0; i < i1; i++) n_eq += (uint32_t)(sh.kr[i] >> 32) == thr ? 1u : 0u;
-                r = block_excl_scan(n_eq, sh.scan, tot);
-            }
-            uint64_t take = 0;
+            uint64_t gtm = 0, eqm = 0;
+#pragma unroll 4
             for (uint32_t i = i0; i < i1; i += 2) {
                 const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const uint32_t k = x[2 * h + 1];
-                    const bool in = i + h < i1;
-                    const bool eq = in && k == thr;
-                    const bool t = in && (k > thr || (eq && (!cut_ties || r < m_eq)));
-                    take |= (uint64_t)(t ? 1u : 0u) << (i + h - i0);
-                    r += eq ? 1u : 0u;
+                    const uint64_t bit = (i + h < i1 ? 1ull : 0ull) << (i + h - i0);
+                    gtm |= k > thr ? bit : 0ull;
+                    eqm |= k == thr ? bit : 0ull;
                 }
             }
-            const uint32_t n_take = (uint32_t)__builtin_popcountll(take);
-            const uint32_t p = block_excl_scan(n_take, sh.scan, tot);
-            // only the threads whose kept rows fall in this split emit; a
-            // kept candidate's position is p plus the kept ones before it
-            // in the thread's mask, so the candidates are independent
-            if ((int64_t)(p + n_take) * kp > start && (int64_t)p * kp < split_end) {
-#pragma unroll 4
-                for (uint32_t i = i0; i < i1; i += 2) {
-                    const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
-                    const uint32_t b = i - i0;
-                    const uint32_t t2 = (uint32_t)(take >> b) & 3u;
-                    const uint32_t pb = p + (uint32_t)__builtin_popcountll(take & ((1ull << b) - 1ull));
-                    if (t2 & 1u) emit(pb, (int32_t)x[0]);
-                    if (t2 & 2u) emit(pb + (t2 & 1u), (int32_t)x[2]);
+            // one scan of both counts (each total < 2^16): the rows at the
+            // threshold before this thread's, and the rows above it
+            const uint32_t n_gt = (uint32_t)__builtin_popcountll(gtm), n_eq = (uint32_t)__builtin_popcountll(eqm);
+            uint32_t tot;
+            const uint32_t pk = block_excl_scan((n_eq << 16) | n_gt, sh.scan, tot);
+            const uint32_t gt_before = pk & 0xFFFFu, eq_before = pk >> 16;
+            // the lowest rows at the threshold are kept, m_eq of them in all
+            const uint32_t eq_keep = eq_before >= m_eq ? 0u : (m_eq - eq_before < n_eq ? m_eq - eq_before : n_eq);
+            uint64_t take = gtm;
+            {
+                uint64_t e = eqm;
+                for (uint32_t j = 0; j < eq_keep; j++) {
+                    const uint64_t low = e & (~e + 1ull);
+                    take |= low;
+                    e ^= low;
                 }
+            }
+            // kept rows before this thread's: its first position
+            sh.epos[tid] = gt_before + (eq_before < m_eq ? eq_before : m_eq);
+            sh.etake[tid] = take;
+            __syncthreads();
+            // each token position of the split below the kept pools: the
+            // thread owning its kept row (the last whose first position is
+            // not past it), then the row's set bit in that thread's mask
+            const int32_t lim = split_end < (int32_t)keep * kp ? split_end : (int32_t)keep * kp;
+            for (int32_t P = start + tid; P < lim; P += 256) {
+                const uint32_t j = kp == 1 ? (uint32_t)P : (uint32_t)P / (uint32_t)kp;
+                int t = 0;
+#pragma unroll
+                for (int st = 128; st > 0; st >>= 1)
+                    if (sh.epos[t + st] <= j) t += st;
+                uint32_t k = j - sh.epos[t];
+                const uint64_t m = sh.etake[t];
+                uint32_t w32 = (uint32_t)m, bit = 0;
+                const uint32_t c32 = (uint32_t)__builtin_popcount(w32);
+                if (k >= c32) {
+                    k -= c32;
+                    w32 = (uint32_t)(m >> 32);
+                    bit = 32;
+                }
+#pragma unroll
+                for (int half = 16; half > 0; half >>= 1) {
+                    const uint32_t c = (uint32_t)__builtin_popcount(w32 & ((1u << half) - 1u));
+                    if (k >= c) {
+                        k -= c;
+                        w32 >>= half;
+                        bit += half;
+                    }
+                }
+                const int32_t r = (int32_t)(uint32_t)sh.kr[per * (uint32_t)t + bit];
+                sidx[P - start] = kp == 1 ? r : r * kp + (int32_t)((uint32_t)P - j * (uint32_t)kp);
             }
         } else {
             uint32_t eq_done = 0, out_done = 0;
