@@ -6,10 +6,12 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "dsa.h"
 #include "dsa_plan.h"
@@ -120,6 +122,40 @@ bool test_fail_launch() {
     const char *e = std::getenv("DSA_TEST_FAIL_LAUNCH");
     return e && e[0] == '1';
 }
+
+// DSA_DUMP_SEL=<path>: every call that selects appends its queries'
+// selections to <path>, one line per query (format in dsa.h).  The file is
+// opened before anything is enqueued and written once the work is done.
+struct SelDump {
+    FILE *f = nullptr;
+    ~SelDump() {
+        if (f) std::fclose(f);
+    }
+    int open() {
+        const char *path = std::getenv("DSA_DUMP_SEL");
+        if (!path || !*path) return DSA_OK;
+        f = std::fopen(path, "a");
+        return f ? (int)DSA_OK : fail(DSA_ERR_ARG, std::string("DSA_DUMP_SEL: cannot open ") + path);
+    }
+    int write(const dsa_batch *b, const int32_t *sel, int32_t sel_ld, const int32_t *cnt, hipStream_t st) {
+        if (!f) return DSA_OK;
+        const size_t n = (size_t)b->n_q;
+        std::vector<int32_t> hs(n * sel_ld), hc(n), hv(n);
+        if (hipStreamSynchronize(st) != hipSuccess ||
+            hipMemcpy(hs.data(), sel, hs.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(hc.data(), cnt, n * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(hv.data(), b->q_nvis, n * 4, hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(DSA_ERR_LAUNCH, "DSA_DUMP_SEL: reading the selection back failed");
+        for (size_t q = 0; q < n; q++) {
+            std::fprintf(f, "q=%zu nvis=%d count=%d:", q, hv[q], hc[q]);
+            const int32_t c = hc[q] < 0 ? 0 : (hc[q] > sel_ld ? sel_ld : hc[q]);
+            for (int32_t i = 0; i < c; i++) std::fprintf(f, " %d", hs[q * sel_ld + i]);
+            std::fputc('\n', f);
+        }
+        std::fflush(f);
+        return DSA_OK;
+    }
+};
 
 dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p) {
     dsa::Args a;
@@ -280,6 +316,8 @@ int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int
         if (sel_ld < p.sel_max) return fail(DSA_ERR_ARG, "sel_ld < top_k + kpool - 1");
         DSA_TRY(check_ws(p, ws, ws_bytes));
         if (test_fail_launch()) return fail(DSA_ERR_LAUNCH, "injected launch failure (DSA_TEST_FAIL_LAUNCH)");
+        SelDump dump;
+        DSA_TRY(dump.open());
         dsa::Args a = base_args(g, b, p);
         bind_workspace(a, p, ws);
         a.scores_in = scores;
@@ -289,7 +327,8 @@ int dsa_topk(const dsa_geometry *g, const dsa_batch *b, const float *scores, int
         a.sel_count = sel_count;
         DSA_TRY(launched(dsa::launch_hist(a, stream), "hist"));
         if (!a.select_scan) DSA_TRY(launched(dsa::launch_filter(a, stream), "filter"));
-        return launched(dsa::launch_select(a, stream), "select");
+        DSA_TRY(launched(dsa::launch_select(a, stream), "select"));
+        return dump.write(b, sel, sel_ld, sel_count, stream);
     });
 }
 
@@ -353,6 +392,8 @@ int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, 
                  const float *idx_w, const dsa_bf16 *idx_k, int64_t key_seq_stride, const dsa_bf16 *q,
                  const dsa_bf16 *cache, int64_t cache_seq_stride, int32_t *sel, int32_t sel_ld, int32_t *sel_count,
                  float *out, float *lse, void *ws, hipStream_t stream) {
+    SelDump dump;
+    DSA_TRY(dump.open());
     dsa::Args a = base_args(g, b, p);
     bind_workspace(a, p, ws);
     uint8_t *w = static_cast<uint8_t *>(ws);
@@ -381,7 +422,7 @@ int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, 
     // decode batches select inside the attention (k_attend_sel); a prefill
     // chunk keeps k_select
     a.attn_sel = p.attn_sel && !a.prefill ? 1 : 0;
-    a.sel_export = sel ? 1 : 0;
+    a.sel_export = sel || dump.f ? 1 : 0;
     // the scorer's histograms feed k_filter, or k_select's own scan; the
     // in-attention scan builds its own
     a.hist_on = (a.attn_sel && a.select_scan) ? 0 : 1;
@@ -393,7 +434,7 @@ int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, 
     if (!a.attn_sel) DSA_TRY(launched(dsa::launch_select(a, stream, ev[4], ev[5]), "select"));
     DSA_TRY(launched(dsa::launch_attend(a, stream, g_events ? ev + 6 : nullptr), "attend"));
     g_ran = 1 | (a.select_scan ? 0 : 2) | (a.attn_sel ? 0 : 4) | 8 | (a.n_split > 1 ? 16 : 0);
-    return (int)DSA_OK;
+    return dump.write(b, a.sel, a.sel_ld, a.sel_count, stream);
 }
 
 }  // namespace

@@ -63,6 +63,18 @@
  *    [0, top_k + kpool - 1] makes the attention of that query NaN, and a
  *    query left with no row gets NaN too.  No such value causes an
  *    out-of-bounds access.
+ *  - Selection dump (a debugging aid for comparing selections line by line
+ *    with another implementation, as the WASTE page does with its DSA dump,
+ *    section "What is checked"): with the environment variable DSA_DUMP_SEL
+ *    set to a file path, dsa_topk, dsa_decode_step and
+ *    dsa_decode_step_noalloc open that file for appending before they
+ *    enqueue anything (DSA_ERR_ARG if it cannot be opened), then wait for
+ *    their stream and append one line per query:
+ *        q=<query> nvis=<visible count> count=<selection count>: <tokens>
+ *    with the selected token indices in ascending order, separated by
+ *    spaces.  The fused steps report their selection even when the caller
+ *    passes no selection buffer.  The wait makes such calls synchronous and
+ *    unusable under graph capture (DSA_ERR_LAUNCH there).
  */
 #ifndef DSA_H
 #define DSA_H
