@@ -1774,10 +1774,15 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
     const uint32_t voff = 16 * lane;
     const uint32_t wb_lds = __builtin_amdgcn_readfirstlane(lds_addr(wb));
     const uint64_t c_base = reinterpret_cast<uint64_t>(C), z_base = reinterpret_cast<uint64_t>(kZeroRow);
-    // address of row t, or of the zero row for t outside [0, cache_stride)
-    const int64_t cstride = a.cache_stride;
-    auto row_ok = [cstride](int32_t t) { return t >= 0 && (int64_t)t < cstride; };
-    auto row_addr = [&](int32_t t) -> uint64_t { return row_ok(t) ? c_base + (uint64_t)(uint32_t)t * (2 * D) : z_base; };
+    // address of row t, or of the zero row for t outside [0, cache_stride),
+    // without a branch: one unsigned 32-bit compare (a negative t is a huge
+    // unsigned value) and a mask
+    const uint32_t rlim = a.cache_stride >= (int64_t)0x80000000u ? 0x80000000u : (uint32_t)a.cache_stride;
+    auto row_ok = [rlim](int32_t t) { return (uint32_t)t < rlim; };
+    auto row_addr = [&](int32_t t) -> uint64_t {
+        const uint64_t m = (uint64_t)0 - (uint64_t)row_ok(t);
+        return ((c_base + (uint64_t)(uint32_t)t * (2 * D)) & m) | (z_base & ~m);
+    };
     // lane & 15 holds the index of row lane & 15 of the wave's step j
     auto idx_v = [&](int j) -> int32_t { return j < nj ? sidx[kWvRows * (w + 4 * j) + (lane & 15)] : -1; };
     auto issue = [&](int j, int32_t iv, int b) {
