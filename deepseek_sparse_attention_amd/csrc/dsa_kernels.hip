@@ -1244,15 +1244,12 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
-// The same with a uniform base address in SGPRs and a per-lane 32-bit offset
-// (the base is passed through readfirstlane, which keeps it in SGPRs for the
-// asm operand wherever the compiler cannot prove it uniform).
-__device__ __forceinline__ void dma16s(const void *base_in, uint32_t off, uint32_t lds) {
-    const uint64_t bi = reinterpret_cast<uint64_t>(base_in);
-    const uint64_t bu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bi) |
-                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bi >> 32)) << 32);
-    const void *base = reinterpret_cast<const void *>(bu);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+// The same with a uniform base address in SGPRs and a per-lane 32-bit
+// offset.  The base is read out of a lane by v_readlane just before: a VALU
+// write of an SGPR that a VMEM instruction reads needs five wait states (the
+// compiler does not see the read inside the asm), hence s_nop 4.
+__device__ __forceinline__ void dma16u(uint64_t base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -1787,10 +1784,15 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
     auto idx_v = [&](int j) -> int32_t { return j < nj ? sidx[kWvRows * (w + 4 * j) + (lane & 15)] : -1; };
     auto issue = [&](int j, int32_t iv, int b) {
         const uint32_t vb = wb_lds + b * Cfg::BUF;
+        // the step's 16 row addresses at once (lane r: row r), then each
+        // row's DMA from its two halves read out of lane r
+        const uint64_t av = row_addr(iv);
+        const uint32_t alo = (uint32_t)av, ahi = (uint32_t)(av >> 32);
 #pragma unroll
         for (int r = 0; r < kWvRows; r++) {
-            const int32_t t = __builtin_amdgcn_readlane(iv, r);
-            dma16s(reinterpret_cast<const void *>(row_addr(t)), voff, vb + r * Cfg::VS);
+            const uint64_t base = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)alo, r) |
+                                  ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ahi, r) << 32);
+            dma16u(base, voff, vb + r * Cfg::VS);
         }
         if constexpr (D > 512) {
 #pragma unroll
