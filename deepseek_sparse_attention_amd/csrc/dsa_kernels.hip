@@ -1910,66 +1910,70 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
         wait_vm<0>();
     }
 
-    // merge the four waves: each writes its (max, sum, O) to LDS; after one
-    // barrier every wave combines a quarter of the columns
+    // merge the four waves: wave w finishes column blocks 8w .. 8w + 7 of
+    // the 16 heads.  Each wave's (max, sum) and the column blocks it does
+    // not finish go to LDS; after one barrier a wave combines its own blocks,
+    // still in registers, with the other three waves' from LDS, in the
+    // accumulator layout (lane (g, n): head n, columns 16 cb + 4 g .. + 3).
     const float l_w = xor32_sum(xor16_sum(l_part));
     if (g == 0) {
         smx[w][n] = m_ref;
         ssum[w][n] = l_w;
     }
     __syncthreads();   // every wave is past its last LDS read of the row buffers
+    float *const sbase = reinterpret_cast<float *>(lds);
     {
-        float *so = reinterpret_cast<float *>(lds) + w * 16 * Cfg::OS + n * Cfg::OS + 4 * g;
+        float *so = sbase + (w * 16 + n) * Cfg::OS + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < 32; cb++) *(f32x4 *)(so + 16 * cb) = acc[cb];
+        for (int cb = 0; cb < 32; cb++)
+            if ((cb >> 3) != w) *(f32x4 *)(so + 16 * cb) = acc[cb];
     }
     __syncthreads();
-    const float *sb = reinterpret_cast<const float *>(lds);
-    // lane: heads 4k + lane / 16 (k = 0..3), columns 128 w + 64 h + 4 (lane & 15) (h = 0, 1)
-    float fk[4][4], Lk[4], Mk[4];
+    float fk[4], M = -INFINITY, L = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const int hh = 4 * k + (lane >> 4);
-        float M = -INFINITY;
+    for (int ww = 0; ww < 4; ww++) M = fmaxf(M, smx[ww][n]);
 #pragma unroll
-        for (int ww = 0; ww < 4; ww++) M = fmaxf(M, smx[ww][hh]);
-        float L = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ww++) {
-            const float mw = smx[ww][hh];
-            fk[k][ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            L += ssum[ww][hh] * fk[k][ww];
-        }
-        Mk[k] = M;
-        Lk[k] = L;
+    for (int ww = 0; ww < 4; ww++) {
+        const float mw = smx[ww][n];
+        fk[ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        L += ssum[ww][n] * fk[ww];
     }
+    const int hd = 16 * hg + n;
+    const bool bad = invalid || L == 0.f;
+    const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + hd;
+    // the wave index is uniform: one copy of the finish per wave, so that
+    // its own accumulators are indexed statically
+    auto finish = [&](auto wtag) {
+        constexpr int W = decltype(wtag)::value;
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const int hh = 4 * k + (lane >> 4), hd = 16 * hg + hh;
-        const float L = Lk[k];
-        const bool bad = invalid || L == 0.f;
+        for (int i = 0; i < 8; i++) {
+            const int cb = 8 * W + i, col = 16 * cb + 4 * g;
+            f32x4 v = acc[cb] * fk[W];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int col = 128 * w + 64 * h + 4 * (lane & 15);
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ww = 0; ww < 4; ww++) v += *(const f32x4 *)(sb + (ww * 16 + hh) * Cfg::OS + col) * fk[k][ww];
+            for (int ww = 0; ww < 4; ww++)
+                if (ww != W) v += *(const f32x4 *)(sbase + (ww * 16 + n) * Cfg::OS + col) * fk[ww];
             if (a.n_split == 1) {
                 const f32x4 o = bad ? f32x4{NAN, NAN, NAN, NAN} : v * (1.f / L);
                 *(f32x4 *)(a.out + ((size_t)q * kHeads + hd) * kLatent + col) = o;
             } else {
-                const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + hd;
                 *(f32x4 *)(a.pacc + slot * kLatent + col) = v;
             }
         }
-        if (w == 0 && (lane & 15) == 0) {
-            if (a.n_split == 1) {
-                if (a.lse) a.lse[(size_t)q * kHeads + hd] = bad ? NAN : (Mk[k] + __log2f(L)) * 0.69314718055994531f;
-            } else {
-                const size_t slot = ((size_t)q * a.n_split + sp) * kHeads + hd;
-                a.pml[2 * slot] = Mk[k];
-                a.pml[2 * slot + 1] = L;
-            }
+    };
+    if (w == 0)
+        finish(std::integral_constant<int, 0>());
+    else if (w == 1)
+        finish(std::integral_constant<int, 1>());
+    else if (w == 2)
+        finish(std::integral_constant<int, 2>());
+    else
+        finish(std::integral_constant<int, 3>());
+    if (w == 0 && g == 0) {
+        if (a.n_split == 1) {
+            if (a.lse) a.lse[(size_t)q * kHeads + hd] = bad ? NAN : (M + __log2f(L)) * 0.69314718055994531f;
+        } else {
+            a.pml[2 * slot] = M;
+            a.pml[2 * slot + 1] = L;
         }
     }
 }
