@@ -1897,7 +1897,14 @@ __device__ __forceinline__ void wv_rows(const Args &a, uint8_t *lds, const int32
                 for (int c = 0; c < 32; c++) asm volatile("" ::"v"(t[c]));
 #pragma unroll
                 for (int c = 0; c < 32; c++) {
-                    const i16x8 tv = {t[c][0], t[c][1], t[c][2], t[c][3], t[c][0], t[c][1], t[c][2], t[c][3]};
+                    // the four V values twice (K = 16 rows x {hi, lo} of P):
+                    // one v_mov_b64 (the compiler copies the pair with two
+                    // v_mov_b32; fused attention at 8 x 128K 19.7 vs 20.2 us)
+                    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+                    const uint64_t t64 = __builtin_bit_cast(uint64_t, t[c]);
+                    uint64_t d64;
+                    asm("v_mov_b64 %0, %1" : "=v"(d64) : "v"(t64));
+                    const u64x2 tv = {t64, d64};
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tv), pb, acc[c], 0, 0, 0);
                 }
             }
