@@ -1322,14 +1322,20 @@ __global__ __launch_bounds__(512) void k_attend(Args a) {
     // w+16, w+24; waves 0..3 also the RoPE tails of rows 8w..8w+7.  iv holds
     // the step's row index of lane & 31, ir that of row 8w + lane / 8.
     const bool rope_wave = D > 512 && w < 4;
+    const uint64_t c_base = reinterpret_cast<uint64_t>(C), z_base = reinterpret_cast<uint64_t>(kZeroRow);
     auto issue = [&](int32_t iv, int32_t ir, int b) {
         uint8_t *vb = lds + b * Cfg::BUF;
+        // the step's row addresses at once (lane r: row r, the zero row for
+        // t < 0), then each of this wave's rows from two lane reads
+        const uint64_t m = (uint64_t)(int64_t)(iv >> 31);
+        const uint64_t av = ((c_base + (uint64_t)(uint32_t)iv * (2 * D)) & ~m) | (z_base & m);
+        const uint32_t alo = (uint32_t)av, ahi = (uint32_t)(av >> 32);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int r = w + 8 * i;
-            const int32_t t = __builtin_amdgcn_readlane(iv, r);
-            const uint8_t *src = t >= 0 ? C + (size_t)t * (2 * D) : kZeroRow;
-            dma16(src + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(vb + r * Cfg::VS)));
+            const uint64_t base = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)alo, r) |
+                                  ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ahi, r) << 32);
+            dma16u(base, 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(vb + r * Cfg::VS)));
         }
         if (rope_wave) {
             const int row = 8 * w + (lane >> 3);
