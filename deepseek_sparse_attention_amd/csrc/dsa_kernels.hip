@@ -2270,20 +2270,30 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
         __syncthreads();
         const uint32_t pre2 = (b1 << 10) | b2;
         const uint32_t need3 = keep - above1 - above2;
-        // third digit: the candidates of bucket (b1, b2), eight reads in
-        // flight per thread
+        // thread t takes candidates [per t, per (t + 1)), in row order (per
+        // a multiple of 2 and <= 48, so that its candidates fit 64-bit
+        // masks; read two at a time).  One pass over them settles all but
+        // the candidates of bucket (b1, b2): those above its two-digit
+        // prefix are kept (gtm), those below dropped; the bucket's go to
+        // the third-digit histogram and are marked (unc) for a second look
+        // once the threshold is known.
+        const uint32_t per = ((n_cand + 255) / 256 + 1) & ~1u;
+        const uint32_t i0 = per * tid, i1 = i0 + per < n_cand ? i0 + per : n_cand;
+        uint64_t gtm = 0, unc = 0;
         if (in_lds) {
-            for (uint32_t i0 = 0; i0 < n_cand; i0 += 256 * 8) {
-                uint32_t k[8];
+#pragma unroll 4
+            for (uint32_t i = i0; i < i1; i += 2) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
 #pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const uint32_t i = i0 + tid + 256 * u;
-                    k[u] = i < n_cand ? (uint32_t)(sh.kr[i] >> 32) : 0u;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const uint32_t i = i0 + tid + 256 * u;
-                    if (i < n_cand && (k[u] >> 10) == pre2) atomicAdd(&sh.h3[k[u] & 1023], 1u);
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t k = x[2 * h + 1];
+                    const bool in = i + h < i1;
+                    const uint64_t bit = 1ull << (i + h - i0);
+                    gtm |= in && (k >> 10) > pre2 ? bit : 0ull;
+                    if (in && (k >> 10) == pre2) {
+                        unc |= bit;
+                        atomicAdd(&sh.h3[k & 1023], 1u);
+                    }
                 }
             }
         } else {
@@ -2296,22 +2306,13 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
         const uint32_t m_eq = need3 - above3;         // rows equal to thr kept, lowest rows first
 
         if (in_lds) {
-            // thread t ranks candidates [per t, per (t + 1)), in row order
-            // (per a multiple of 2 and <= 48, so that its candidates above
-            // and at the threshold fit 64-bit masks; read two at a time)
-            const uint32_t per = ((n_cand + 255) / 256 + 1) & ~1u;
-            const uint32_t i0 = per * tid, i1 = i0 + per < n_cand ? i0 + per : n_cand;
-            uint64_t gtm = 0, eqm = 0;
-#pragma unroll 4
-            for (uint32_t i = i0; i < i1; i += 2) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.kr[i]);
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const uint32_t k = x[2 * h + 1];
-                    const uint64_t bit = (i + h < i1 ? 1ull : 0ull) << (i + h - i0);
-                    gtm |= k > thr ? bit : 0ull;
-                    eqm |= k == thr ? bit : 0ull;
-                }
+            // the bucket's candidates against the threshold
+            uint64_t eqm = 0;
+            for (uint64_t u = unc; u; u &= u - 1ull) {
+                const uint32_t bi = (uint32_t)__builtin_ctzll(u);
+                const uint32_t k = (uint32_t)(sh.kr[i0 + bi] >> 32);
+                gtm |= k > thr ? 1ull << bi : 0ull;
+                eqm |= k == thr ? 1ull << bi : 0ull;
             }
             // one scan of both counts (each total < 2^16): the rows at the
             // threshold before this thread's, and the rows above it
