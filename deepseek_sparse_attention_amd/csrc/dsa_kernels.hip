@@ -699,14 +699,6 @@ __global__ __launch_bounds__(256) void k_hist(Args a) {
 //     the query's histogram, the only state that must be zero between calls.
 // No global atomics: chunks own their candidate slots.
 
-__device__ __forceinline__ void load_hist(const uint32_t *gh, uint32_t *lh) {
-    uint32_t v[kHistBins / 256];
-#pragma unroll
-    for (int i = 0; i < kHistBins / 256; i++) v[i] = gh[threadIdx.x + 256 * i];
-#pragma unroll
-    for (int i = 0; i < kHistBins / 256; i++) lh[threadIdx.x + 256 * i] = v[i];
-}
-
 // n scores from s[r0..r0+n) (rows at or past r1 read as 0); 16-byte loads
 // when the run is aligned and whole.
 template <int N>
@@ -733,26 +725,45 @@ __device__ __forceinline__ void load_scores(const float *s, int64_t r0, int64_t 
 template <int kFiltPer>
 __global__ __launch_bounds__(256) void k_filter(Args a) {
     constexpr int kFiltBlock = 256 * kFiltPer;
-    __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t scan[8];
     __shared__ uint32_t res[4];
     const int q = blockIdx.y, c = blockIdx.x;
-    const QInfo qi = query_info(a, q);
-    if (qi.mode != 1) return;
-    const int64_t rows = qi.rows;
-    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-    if (c >= nch) return;
+    // The query's first-digit histogram (thread t: bins 4095 - 16 t - i,
+    // four 16-byte loads) and the chunk's first block of scores are
+    // requested before the query's fields return: one round trip, not two.
+    // The block is read up to the score row's length (score_ld entries);
+    // rows at or past the query's own are not used.
     const float *s = a.scores_in + (size_t)q * a.score_ld;
     const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
     const int64_t r0 = (int64_t)c * a.chunk;
-    const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
-    // first block of scores in flight while the threshold bucket is found
     float sv[kFiltPer];
-    load_scores<kFiltPer>(s, r0 + kFiltPer * threadIdx.x, r1, vec, sv);
-    load_hist(a.hist + (size_t)q * kHistStride, hist);
-    __syncthreads();
+    load_scores<kFiltPer>(s, r0 + kFiltPer * threadIdx.x, r0 + a.chunk < a.score_ld ? r0 + a.chunk : a.score_ld, vec,
+                          sv);
+    u32x4 hv[4];
+    {
+        const uint32_t *gh = a.hist + (size_t)q * kHistStride + (kHistBins - 16 * (threadIdx.x + 1));
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = *(const u32x4 *)(gh + 4 * j);
+    }
+    // a wave leaving without using them waits for those loads first
+    auto drain = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    const QInfo qi = query_info(a, q);
+    if (qi.mode != 1) {
+        drain();
+        return;
+    }
+    const int64_t rows = qi.rows;
+    const int nch = (int)((rows + a.chunk - 1) / a.chunk);
+    if (c >= nch) {
+        drain();
+        return;
+    }
+    const int64_t r1 = r0 + a.chunk < rows ? r0 + a.chunk : rows;
+    uint32_t hc[16];   // hc[i]: bin 4095 - 16 t - i
+#pragma unroll
+    for (int i = 0; i < 16; i++) hc[i] = hv[(15 - i) >> 2][(15 - i) & 3];
     uint32_t above1;
-    const uint32_t b1 = find_bucket<kHistBins>(hist, (uint32_t)a.keep, scan, res, above1);
+    const uint32_t b1 = bucket_from_regs<16>(hc, (uint32_t)a.keep, scan, res, above1);
     if (c == 0 && threadIdx.x == 0) {
         a.thr[2 * q] = b1;
         a.thr[2 * q + 1] = above1;
