@@ -2499,25 +2499,28 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
 // and merged online (running max, rescaled sums).
 __global__ __launch_bounds__(128) void k_reduce(Args a) {
     constexpr int MB = 16;
-    const int q = blockIdx.y, h = blockIdx.x;
-    const QInfo qi = query_info(a, q);
+    const int q = blockIdx.y, h = blockIdx.x, lane = lane_id();
     const size_t slot0 = (size_t)q * a.n_split * kHeads + h;
     float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < a.n_split; s0 += MB) {
+        const int nb = a.n_split - s0 < MB ? a.n_split - s0 : MB;
+        // every load of the round in flight before any use: lane i < nb
+        // reads split s0 + i's (max, sum) (a vector load, so that no
+        // scalar-load wait sits between them), every thread its four
+        // columns of each split's partial
+        float2 ml = {-INFINITY, 0.f};
+        if (lane < nb) ml = *(const float2 *)(a.pml + 2 * (slot0 + (size_t)(s0 + lane) * kHeads));
         f32x4 v[MB];
+#pragma unroll
+        for (int i = 0; i < MB; i++)
+            v[i] = i < nb ? *(const f32x4 *)(a.pacc + (slot0 + (size_t)(s0 + i) * kHeads) * kLatent + 4 * threadIdx.x)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
         float m[MB], l[MB];
 #pragma unroll
         for (int i = 0; i < MB; i++) {
-            m[i] = -INFINITY;
-            l[i] = 0.f;
-            v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (s0 + i < a.n_split) {
-                const size_t slot = slot0 + (size_t)(s0 + i) * kHeads;
-                m[i] = a.pml[2 * slot];
-                l[i] = a.pml[2 * slot + 1];
-                v[i] = *(const f32x4 *)(a.pacc + slot * kLatent + 4 * threadIdx.x);
-            }
+            m[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ml.x), i));
+            l[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ml.y), i));
         }
         float Mn = M;
 #pragma unroll
@@ -2534,6 +2537,7 @@ __global__ __launch_bounds__(128) void k_reduce(Args a) {
         }
         M = Mn;
     }
+    const QInfo qi = query_info(a, q);
     const bool bad = qi.mode == 2 || L == 0.f;
     o = bad ? f32x4{NAN, NAN, NAN, NAN} : o * (1.f / L);
     *(f32x4 *)(a.out + ((size_t)q * kHeads + h) * kLatent + 4 * threadIdx.x) = o;
