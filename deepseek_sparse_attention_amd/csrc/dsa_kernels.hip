@@ -2142,9 +2142,43 @@ __device__ __forceinline__ void as_hist_pass(const float *s, bool vec, int64_t r
 // count.  With write_sel the same positions go to sel (and, for the last
 // split, the padding after the splits up to sel_ld; for the first split the
 // count).  Returns the selection count.  All 256 threads call it.
+// The filter-mode selection's first loads, issued at the kernel's start,
+// before the query's fields return (none of them depends on those): the
+// threshold bucket b1 and the rows above it (k_filter), the second-digit
+// histogram of bucket b1 (thread t: bins 1023 - 4t - i), the chunk
+// candidate counts (thread t: chunks 4t .. 4t + 3; lane l of wave w also
+// chunk w + 4 (l % 16)), and the first 128 slots of the wave's chunks
+// w + 4u, read before the counts say how many are filled.  The plan's chunk
+// count bounds them; as_select drops what lies past the query's own.
+constexpr int kAsU = 16;
+struct AsPre {
+    u32x4 sv[kAsU];
+    uint32_t cw, c4[4], h4[4], b1, above1;
+};
+
+__device__ __forceinline__ void as_preload(const Args &a, int q, AsPre &p) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint64_t *cq = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
+    const uint32_t *cc = a.chunk_cnt + (size_t)q * a.n_chunks;
+    const uint32_t *gh2 = a.hist + (size_t)q * kHistStride + kHistH2;
+#pragma unroll
+    for (int u = 0; u < kAsU; u++) {
+        const int c = w + 4 * u;
+        p.sv[u] = c < a.n_chunks ? *(const u32x4 *)(cq + (size_t)c * a.cand_cap + 2 * lane) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int cl = w + 4 * (lane & 15);
+    p.cw = cl < a.n_chunks ? cc[cl] : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) p.c4[i] = 4 * tid + i < a.n_chunks ? cc[4 * tid + i] : 0u;
+    p.b1 = a.thr[2 * q];
+    p.above1 = a.thr[2 * q + 1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) p.h4[i] = gh2[1023 - 4 * tid - i];
+}
+
 template <bool SCAN, class IssueQ>
 __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_t *sidx, int q, const QInfo &qi,
-                                             int sp, bool write_sel, IssueQ issue_q) {
+                                             int sp, bool write_sel, IssueQ issue_q, const AsPre &pre) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int kp = a.kpool;
     const int32_t start = sp * a.split_rows, split_end = start + a.split_rows;
@@ -2205,34 +2239,20 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
             __syncthreads();
             b2 = find_bucket<1024>(sh.h2, keep - above1, sh.scan, sh.res, above2);
         } else {
-            // One round trip brings the threshold bucket b1 and the rows
-            // above it (k_filter), the second-digit histogram of bucket b1
-            // (k_filter's; thread t: bins 1023 - 4t - i), the chunk candidate
-            // counts (thread t: chunks 4t .. 4t + 3; lane l of wave w also
-            // chunk w + 4 (l % 16)), and the first 128 slots of the wave's
-            // chunks w + 4u, read before the counts say how many are filled.
-            // The queries follow.
+            // the preloaded round trip (as_preload); chunks past the
+            // query's own are dropped
             const int nch = (int)((rows + a.chunk - 1) / a.chunk);
-            const uint32_t *cc = a.chunk_cnt + (size_t)q * a.n_chunks;
-            const uint32_t *gh2 = a.hist + (size_t)q * kHistStride + kHistH2;
             const uint64_t *cq = a.cand + (size_t)q * a.n_chunks * a.cand_cap;
-            constexpr int kU = 16;
-            u32x4 sv[kU];
-#pragma unroll
-            for (int u = 0; u < kU; u++) {
-                const int c = w + 4 * u;
-                sv[u] = c < nch ? *(const u32x4 *)(cq + (size_t)c * a.cand_cap + 2 * lane) : u32x4{0u, 0u, 0u, 0u};
-            }
+            constexpr int kU = kAsU;
+            const u32x4 *sv = pre.sv;
             const int cl = w + 4 * (lane & 15);
-            const uint32_t cw = cl < nch ? cc[cl] : 0u;
+            const uint32_t cw = cl < nch ? pre.cw : 0u;
             uint32_t c4[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) c4[i] = 4 * tid + i < nch ? cc[4 * tid + i] : 0u;
-            b1 = a.thr[2 * q];
-            above1 = a.thr[2 * q + 1];
-            uint32_t h4[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) h4[i] = gh2[1023 - 4 * tid - i];
+            for (int i = 0; i < 4; i++) c4[i] = 4 * tid + i < nch ? pre.c4[i] : 0u;
+            b1 = pre.b1;
+            above1 = pre.above1;
+            const uint32_t(&h4)[4] = pre.h4;
             issue_q();
             uint32_t run = block_excl_scan(c4[0] + c4[1] + c4[2] + c4[3], sh.scan, n_cand);
 #pragma unroll
@@ -2456,6 +2476,8 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
     const int hg = blockIdx.x / pairs8, pair = blockIdx.x % pairs8;
     if (pair >= pairs) return;
     const int q = pair / a.n_split, sp = pair % a.n_split;
+    AsPre pre;
+    if (!SCAN) as_preload(a, q, pre);
     const QInfo qi = query_info(a, q);
     const int lane = lane_id(), g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2482,7 +2504,7 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
     // workspace's histograms do not match the scores) reads as no row
     for (int r = threadIdx.x; r < a.split_rows; r += 256) sidx[r] = -1;
     AsShared &sh = *reinterpret_cast<AsShared *>(lds);
-    const int32_t count = as_select<SCAN>(a, sh, sidx, q, qi, sp, a.sel_export && hg == 0, issue_q);
+    const int32_t count = as_select<SCAN>(a, sh, sidx, q, qi, sp, a.sel_export && hg == 0, issue_q, pre);
     const bool invalid = qi.mode == 2;
     const int32_t start = sp * a.split_rows;
     const int32_t nrows = count > start ? (count - start < a.split_rows ? count - start : a.split_rows) : 0;
