@@ -81,10 +81,19 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     p.score_ld = (p.max_rows + 63) & ~(int64_t)63;
     p.sel_max = top_k + kpool - 1;
 
-    // top-k chunks: aim at ~512 work-groups over the batch, 1024..65536 rows each
+    // top-k chunks: aim at ~512 work-groups over the batch, 1024..8192 rows
+    // each.  Longer chunks make each k_filter work-group a longer chain of
+    // dependent block loads, and k_select gathers fewer chunks at once
+    // (filter + select, us: the 512-position prefill chunk at 128K 79.6 with
+    // 8192 rows vs 93.7 with 65536; 128 queries at 128K 28.3 vs 34.8 with
+    // 32768; 64 queries 21.5 vs 24.8 with 16384)
     int64_t want = (p.max_rows * (int64_t)n_q) / 512;
     int64_t ch = 1024;
-    while (ch < want && ch < 65536) ch <<= 1;
+    while (ch < want && ch < 8192) ch <<= 1;
+    if (const char *e = getenv("DSA_TOPK_CHUNK")) {   // tuning override: a power of two, 1024 .. 65536
+        const int t = atoi(e);
+        if (t >= 1024 && t <= 65536 && (t & (t - 1)) == 0) ch = t;
+    }
     while ((p.max_rows + ch - 1) / ch > kMaxChunks) ch <<= 1;
     p.chunk = (int32_t)ch;
     p.n_chunks = (int32_t)((p.max_rows + ch - 1) / ch);
