@@ -341,6 +341,15 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             vv[i] = __builtin_nontemporal_load((const u32x4 *)(K + r * 256 + 16 * (lane & 15)));
         }
     };
+    // A step's score is stored at the start of the next step, before that
+    // step's key loads: the wait for those loads then leaves no store
+    // younger than them outstanding (waits count completions in issue order,
+    // so a store issued after them would have to complete too).
+    int64_t pend_row = -1;
+    float pend = 0.f;
+    auto flush = [&] {
+        if (pend_row >= 0) srow[pend_row] = pend;
+    };
     // one 64-row step from the registers vv: staged in the LDS tile, vv
     // refilled with the wave's next step (row `ahead`), then scored
     auto step = [&](u32x4 (&vv)[16], int64_t base, int64_t ahead, int64_t end) {
@@ -349,6 +358,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
             const int r = 4 * i + (lane >> 4), pc = lane & 15;
             *(u32x4 *)(tb + r * 256 + 16 * (pc ^ (r & 15))) = vv[i];
         }
+        flush();
         if (ahead < end) fetch(vv, ahead);
         __builtin_amdgcn_wave_barrier();
         float p[4];
@@ -379,10 +389,9 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
         const float q1 = keep1 + __shfl_xor(send1, 16, 64);
         const float score = (b1 ? q1 : q0) + __shfl_xor(b1 ? q0 : q1, 32, 64);
         const int64_t row = base + 16 * st_mine + n;
-        if (row < end) {
-            srow[row] = score;
-            if (hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
-        }
+        pend_row = row < end ? row : -1;
+        pend = score;
+        if (row < end && hist) atomicAdd(&lhist[order_key(score) >> 20], 1u);
     };
     // tiles t0 = blockIdx.x * tile, stepping by the grid (one pass in the
     // common case; the prefill fix-up grid has one work-group per query)
@@ -398,6 +407,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     }
     for (; base < end; base += wstep) step(v, base, base + wstep, end);
     }
+    flush();
     if (hist) {
         __syncthreads();
         uint32_t *gh = a.hist + (size_t)q * kHistStride;
