@@ -423,9 +423,10 @@ int enqueue_step(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &p, 
     // chunk keeps k_select
     a.attn_sel = p.attn_sel && !a.prefill ? 1 : 0;
     a.sel_export = sel || dump.f ? 1 : 0;
-    // the scorer's histograms feed k_filter, or k_select's own scan; the
-    // in-attention scan builds its own
-    a.hist_on = (a.attn_sel && a.select_scan) ? 0 : 1;
+    // the scorer's histograms feed k_filter, k_select's own scan, or the
+    // in-attention scan, which k_reduce then clears; an unsplit in-attention
+    // scan (no k_reduce) builds its own
+    a.hist_on = (a.attn_sel && a.select_scan && a.n_split <= 1) ? 0 : 1;
     hipEvent_t ev[10];
     for (int32_t i = 0; i < 10; i++) ev[i] = timing_event(i);
     g_ran = 0;

@@ -136,11 +136,12 @@ __device__ uint32_t block_sum(uint32_t v, uint32_t *smem) {
 // Radix step: with the counts of NB = 256 PER bins of the items still in
 // play and `need` of them still to take from the top, find the bin b
 // holding the need-th largest: suffix(b) >= need > suffix(b+1).  Returns b,
-// sets above = suffix(b+1).  256 threads; thread t holds in c the counts of
-// the PER bins just below NB - PER*t (c[i]: bin NB - PER t - 1 - i).
+// sets above = suffix(b+1) (and *in_bin = the count of bin b).  256
+// threads; thread t holds in c the counts of the PER bins just below
+// NB - PER*t (c[i]: bin NB - PER t - 1 - i).
 template <int PER>
 __device__ uint32_t bucket_from_regs(const uint32_t (&c)[PER], uint32_t need, uint32_t *smem, uint32_t *res,
-                                     uint32_t &above) {
+                                     uint32_t &above, uint32_t *in_bin = nullptr) {
     const int hi = 256 * PER - PER * (int)threadIdx.x;
     uint32_t s = 0;
 #pragma unroll
@@ -148,7 +149,7 @@ __device__ uint32_t bucket_from_regs(const uint32_t (&c)[PER], uint32_t need, ui
     uint32_t total;
     const uint32_t before = block_excl_scan(s, smem, total);   // items in higher bins
     if (before < need && before + s >= need) {
-        uint32_t run = before, bin = 0, run_at = 0;
+        uint32_t run = before, bin = 0, run_at = 0, cnt = 0;
         bool found = false;
 #pragma unroll
         for (int i = 0; i < PER; i++) {
@@ -156,21 +157,25 @@ __device__ uint32_t bucket_from_regs(const uint32_t (&c)[PER], uint32_t need, ui
                 found = true;
                 bin = (uint32_t)(hi - 1 - i);
                 run_at = run;
+                cnt = c[i];
             }
             run += c[i];
         }
         res[0] = bin;
         res[1] = run_at;
+        res[2] = cnt;
     }
     // fewer than `need` items in all (a histogram that does not match the
     // scores): bin 0, with every item above it counted
     if (threadIdx.x == 255 && before + s < need) {
         res[0] = 0;
         res[1] = before + s - c[PER - 1];
+        res[2] = c[PER - 1];
     }
     __syncthreads();
     above = res[1];
     const uint32_t b = res[0];
+    if (in_bin) *in_bin = res[2];
     __syncthreads();
     return b;
 }
@@ -2219,13 +2224,23 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
         bool in_lds;
         if (SCAN) {
             issue_q();
-            for (int i = tid; i < kHistBins; i += 256) sh.h1[i] = 0;
             for (int i = tid; i < 1024; i += 256) sh.h2[i] = 0;
-            __syncthreads();
-            as_hist_pass(s, vec, rows, 32, 0u, 20, kHistBins, sh.h1);
-            __syncthreads();
-            b1 = find_bucket<kHistBins>(sh.h1, keep, sh.scan, sh.res, above1);
-            n_cand = above1 + sh.h1[b1];
+            if (a.hist_on) {
+                // the scorer's first-digit histogram, read at the kernel's
+                // start (pre.sv[j]: bins 4095 - 16 t - 4 j - 3 .. + 3)
+                uint32_t hc[16], in_b1;
+#pragma unroll
+                for (int i = 0; i < 16; i++) hc[i] = pre.sv[(15 - i) >> 2][(15 - i) & 3];
+                b1 = bucket_from_regs<16>(hc, keep, sh.scan, sh.res, above1, &in_b1);
+                n_cand = above1 + in_b1;
+            } else {
+                for (int i = tid; i < kHistBins; i += 256) sh.h1[i] = 0;
+                __syncthreads();
+                as_hist_pass(s, vec, rows, 32, 0u, 20, kHistBins, sh.h1);
+                __syncthreads();
+                b1 = find_bucket<kHistBins>(sh.h1, keep, sh.scan, sh.res, above1);
+                n_cand = above1 + sh.h1[b1];
+            }
             in_lds = n_cand <= (uint32_t)kAsCap;
             if (in_lds) {
                 as_compact(s, vec, 0, rows, b1, 0u, (uint32_t)kAsCap, sh);
@@ -2487,7 +2502,15 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
     if (pair >= pairs) return;
     const int q = pair / a.n_split, sp = pair % a.n_split;
     AsPre pre;
-    if (!SCAN) as_preload(a, q, pre);
+    if (!SCAN) {
+        as_preload(a, q, pre);
+    } else if (a.hist_on) {
+        // the one-pass top-k takes its first digit from the scorer's
+        // histogram (k_reduce clears it after this kernel)
+        const uint32_t *gh = a.hist + (size_t)q * kHistStride + (kHistBins - 16 * (threadIdx.x + 1));
+#pragma unroll
+        for (int j = 0; j < 4; j++) pre.sv[j] = *(const u32x4 *)(gh + 4 * j);
+    }
     const QInfo qi = query_info(a, q);
     const int lane = lane_id(), g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2532,6 +2555,11 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
 __global__ __launch_bounds__(128) void k_reduce(Args a) {
     constexpr int MB = 16;
     const int q = blockIdx.y, h = blockIdx.x, lane = lane_id();
+    // the fused step's one-pass top-k read the query's first-digit histogram
+    // from the scorer in the kernel before: work-group h clears bins
+    // 64 h .. 64 h + 63 of it for the next call
+    if (a.attn_sel && a.select_scan && a.hist_on && threadIdx.x < kHistBins / kHeads)
+        a.hist[(size_t)q * kHistStride + (kHistBins / kHeads) * h + threadIdx.x] = 0;
     const size_t slot0 = (size_t)q * a.n_split * kHeads + h;
     float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
