@@ -2109,12 +2109,18 @@ static_assert(sizeof(AsShared) <= 4 * WvCfg<512>::WAVE, "the selection fits the 
 // r), in row order, to sh.key / sh.row from position `base` on; entries at
 // or past `limit` are counted but not stored.  Returns the number found.
 __device__ __forceinline__ uint32_t as_compact(const float *s, bool vec, int64_t r0, int64_t r1, uint32_t b1, uint32_t base,
-                               uint32_t limit, AsShared &sh) {
+                               uint32_t limit, AsShared &sh, const u32x4 *first = nullptr) {
     uint32_t found = 0;
     for (int64_t sb = r0; sb < r1; sb += kAsTile) {
         const int64_t rb = sb + kAsPer * threadIdx.x;
         float v[kAsPer];
-        load_scores<kAsPer>(s, rb, r1, vec, v);
+        if (first && sb == r0) {
+            // the first tile's scores, already in registers
+#pragma unroll
+            for (int i = 0; i < kAsPer; i++) v[i] = __uint_as_float(first[i >> 2][i & 3]);
+        } else {
+            load_scores<kAsPer>(s, rb, r1, vec, v);
+        }
         uint32_t keys[kAsPer];
         uint32_t m = 0;
 #pragma unroll
@@ -2243,7 +2249,7 @@ __device__ __forceinline__ int32_t as_select(const Args &a, AsShared &sh, int32_
             }
             in_lds = n_cand <= (uint32_t)kAsCap;
             if (in_lds) {
-                as_compact(s, vec, 0, rows, b1, 0u, (uint32_t)kAsCap, sh);
+                as_compact(s, vec, 0, rows, b1, 0u, (uint32_t)kAsCap, sh, pre.sv + 4);
                 __syncthreads();
                 for (uint32_t i0 = 0; i0 < n_cand; i0 += 256 * 8) {
                     uint32_t k[8];
@@ -2504,12 +2510,23 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
     AsPre pre;
     if (!SCAN) {
         as_preload(a, q, pre);
-    } else if (a.hist_on) {
+    } else {
         // the one-pass top-k takes its first digit from the scorer's
-        // histogram (k_reduce clears it after this kernel)
-        const uint32_t *gh = a.hist + (size_t)q * kHistStride + (kHistBins - 16 * (threadIdx.x + 1));
+        // histogram (k_reduce clears it after this kernel), and the first
+        // kAsTile scores (rows 16 t .. 16 t + 15; read up to the score
+        // row's length, rows past the query's own are not used) go to
+        // registers too
+        if (a.hist_on) {
+            const uint32_t *gh = a.hist + (size_t)q * kHistStride + (kHistBins - 16 * (threadIdx.x + 1));
 #pragma unroll
-        for (int j = 0; j < 4; j++) pre.sv[j] = *(const u32x4 *)(gh + 4 * j);
+            for (int j = 0; j < 4; j++) pre.sv[j] = *(const u32x4 *)(gh + 4 * j);
+        }
+        const float *sq = a.scores_in + (size_t)q * a.score_ld;
+        float v[kAsPer];
+        load_scores<kAsPer>(sq, kAsPer * threadIdx.x, a.score_ld < kAsTile ? a.score_ld : kAsTile,
+                            (reinterpret_cast<uintptr_t>(sq) & 15) == 0, v);
+#pragma unroll
+        for (int i = 0; i < kAsPer; i++) pre.sv[4 + (i >> 2)][i & 3] = __float_as_uint(v[i]);
     }
     const QInfo qi = query_info(a, q);
     const int lane = lane_id(), g = lane >> 4, n = lane & 15;
