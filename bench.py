@@ -63,7 +63,7 @@ def score_kernel_hash() -> str:
     its template line to its closing brace."""
     import hashlib
     src = open(KERNEL_SRC).read()
-    i = src.index("template <bool STRIDE, bool F16>\n__global__ __launch_bounds__(256) void k_score(Args a) {")
+    i = src.index("template <bool STRIDE, bool F16, int NW>\n__global__ __launch_bounds__(64 * NW) void k_score(Args a) {")
     j = src.index("\n}\n", i) + 3
     return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
 

@@ -179,6 +179,7 @@ dsa::Args base_args(const dsa_geometry *g, const dsa_batch *b, const dsa::Plan &
     a.select_scan = p.select_scan;
     a.score_tile = p.score_tile;
     a.score_ilv = p.score_ilv;
+    a.score_waves = p.score_waves;
     a.score_valu = p.score_valu;
     a.prefill = b->q_per_seq_hint >= 2 ? 1 : 0;
     a.pf_run = b->q_per_seq_hint;

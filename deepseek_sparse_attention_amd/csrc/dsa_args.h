@@ -37,7 +37,8 @@ struct Args {
     float *pacc, *pml;
     // plan
     int32_t chunk, n_chunks, cand_cap, split_rows, n_split, score_tile;
-    int32_t score_ilv;   // k_score: a query's work-groups take interleaved 256-row steps
+    int32_t score_ilv;   // k_score: a query's work-groups take interleaved steps of all their waves
+    int32_t score_waves; // k_score: waves per work-group (4 or 8)
     int32_t fused;        // 1: dense queries are not scored, histogram accumulated
     int32_t prefill;      // 1: queries come in runs of pf_run that share a sequence
     int32_t pf_run;       // queries per run (>= 2 when prefill)

@@ -253,8 +253,8 @@ __device__ __forceinline__ f32x4 mfma_idx(bf16x8 a, bf16x8 b, f32x4 c) {
     }
 }
 
-// grid (tiles, n_q), 256 threads.  Wave w of a work-group takes 64-row
-// steps t0 + 64 (w + 4 i).  Keys are read with fully coalesced 16-byte loads
+// grid (tiles, n_q), NW = 4 or 8 waves.  Wave w of a work-group takes
+// 64-row steps t0 + 64 (w + NW i).  Keys are read with fully coalesced 16-byte loads
 // (one wave instruction = 1 KiB = 4 rows), the next step's 16 KiB already in
 // flight in registers while the current one is computed; each step is staged
 // in the wave's own LDS tile with the 16-byte pieces of row r stored at
@@ -267,10 +267,11 @@ __device__ __forceinline__ f32x4 mfma_idx(bf16x8 a, bf16x8 b, f32x4 c) {
 // for k-step s.  D[head][row] lands as lane (g, n) holding heads 4g + r
 // (+16) of row n; the epilogue applies ReLU and the head weights and sums
 // the four lane groups.
-template <bool STRIDE, bool F16>
-__global__ __launch_bounds__(256) void k_score(Args a) {
+template <bool STRIDE, bool F16, int NW>
+__global__ __launch_bounds__(64 * NW) void k_score(Args a) {
+    constexpr int kGroup = 64 * NW;   // rows of one step of all the work-group's waves
     __shared__ uint32_t lhist[kHistBins];
-    __shared__ __attribute__((aligned(16))) uint8_t tiles[4][64 * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[NW][64 * 256];
     const int q = blockIdx.y;
     const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
     u32x4 v[16];
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     const bool early = !STRIDE && a.q_seq == nullptr && rmax >= 1;
     if (early) {
         const uint8_t *K0 = reinterpret_cast<const uint8_t *>(a.idx_k + (size_t)q * a.key_stride * kIdxDim);
-        const int64_t b0 = (a.score_ilv ? 256 * (int64_t)blockIdx.x : (int64_t)blockIdx.x * a.score_tile) + 64 * w;
+        const int64_t b0 = (a.score_ilv ? kGroup * (int64_t)blockIdx.x : (int64_t)blockIdx.x * a.score_tile) + 64 * w;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             int64_t r = b0 + 4 * i + (lane >> 4);
@@ -304,13 +305,13 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     }
     const int64_t rows = qi.rows;
     const bool ilv = !STRIDE && a.score_ilv;
-    if ((int64_t)blockIdx.x * (ilv ? 256 : a.score_tile) >= rows) {
+    if ((int64_t)blockIdx.x * (ilv ? kGroup : a.score_tile) >= rows) {
         drain();
         return;
     }
     const bool hist = a.hist_on != 0;
     if (hist) {
-        for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+        for (int i = threadIdx.x; i < kHistBins; i += kGroup) lhist[i] = 0;
         __syncthreads();
     }
     // the in-attention top-k: k_filter accumulates the second-digit
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     // query's first work-group clears it (what the last call left there)
     if (!STRIDE && a.attn_sel && !a.select_scan && blockIdx.x == 0) {
         uint32_t *h2 = a.hist + (size_t)q * kHistStride + kHistH2;
-        for (int i = threadIdx.x; i < 1024; i += 256) h2[i] = 0;
+        for (int i = threadIdx.x; i < 1024; i += kGroup) h2[i] = 0;
     }
 
     bf16x8 qa[2][4];
@@ -400,8 +401,8 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     };
     // tiles t0 = blockIdx.x * tile, stepping by the grid (one pass in the
     // common case; the prefill fix-up grid has one work-group per query)
-    const int64_t wstep = ilv ? 256 * (int64_t)gridDim.x : 256;
-    for (int64_t t0 = (int64_t)blockIdx.x * (ilv ? 256 : a.score_tile); t0 < rows;
+    const int64_t wstep = ilv ? kGroup * (int64_t)gridDim.x : kGroup;
+    for (int64_t t0 = (int64_t)blockIdx.x * (ilv ? kGroup : a.score_tile); t0 < rows;
          t0 = STRIDE ? t0 + (int64_t)gridDim.x * a.score_tile : rows) {
     const int64_t end = !ilv && t0 + a.score_tile < rows ? t0 + a.score_tile : rows;
     int64_t base = t0 + 64 * w;
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) void k_score(Args a) {
     if (hist) {
         __syncthreads();
         uint32_t *gh = a.hist + (size_t)q * kHistStride;
-        for (int i = threadIdx.x; i < kHistBins; i += 256)
+        for (int i = threadIdx.x; i < kHistBins; i += kGroup)
             if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
     }
 }
@@ -2932,11 +2933,14 @@ hipError_t launch_score_fmt(const Args &a, int64_t max_rows, hipStream_t st, hip
     // in prefill mode k_score only picks up queries outside their block's
     // sequence: one work-group per query, striding over the tiles
     if (a.prefill)
-        DSA_LAUNCH(nullptr, ev1, (k_score<true, F16>), dim3(1, a.n_q), dim3(256), st, a);
+        DSA_LAUNCH(nullptr, ev1, (k_score<true, F16, 4>), dim3(1, a.n_q), dim3(256), st, a);
     else if (!F16 && a.score_valu)
         DSA_LAUNCH(ev0, ev1, k_score_valu, dim3((unsigned)((max_rows + 255) / 256), a.n_q), dim3(256), st, a);
+    else if (a.score_waves == 8)
+        DSA_LAUNCH(ev0, ev1, (k_score<false, F16, 8>),
+                   dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(512), st, a);
     else
-        DSA_LAUNCH(ev0, ev1, (k_score<false, F16>),
+        DSA_LAUNCH(ev0, ev1, (k_score<false, F16, 4>),
                    dim3((unsigned)((max_rows + a.score_tile - 1) / a.score_tile), a.n_q), dim3(256), st, a);
     return hipGetLastError();
 }

@@ -42,6 +42,7 @@ struct Plan {
     int32_t select_scan;          // 1: top-k in one kernel that scans the scores
     int32_t score_tile;           // key rows per score work-group
     int32_t score_ilv;            // score work-groups take interleaved 256-row steps
+    int32_t score_waves;          // waves per score work-group
     int32_t score_valu;           // decode scorer on the vector ALU instead of MFMA
 
     // workspace byte offsets (absolute once place_workspace has run): the
@@ -178,6 +179,15 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     // together (8 x 128K: 44.4 vs 45.6 us); DSA_SCORE_ILV=0/1 forces either.
     p.score_ilv = tile >= 1024 ? 1 : 0;
     if (const char *e = getenv("DSA_SCORE_ILV")) p.score_ilv = atoi(e) != 0;
+    // A batch of at most 256 whole 1,024-row tiles (one or two queries at
+    // 128K, the k-pool query) has one work-group per CU either way: 8 waves
+    // per work-group then keep twice the key steps in flight per CU (C4 38.4
+    // vs 38.8 us per step, one query at 128K 34.0 vs 34.3, two 37.3 vs 37.9);
+    // larger batches keep 4 waves and two work-groups per CU (8 x 128K with
+    // 8 waves: 77.9 vs 73.3 us).  DSA_SCORE_WAVES=4/8 forces either.
+    const int64_t n_tiles = (int64_t)n_q * ((p.max_rows + tile - 1) / tile);
+    p.score_waves = tile >= 1024 && n_tiles <= 256 ? 8 : 4;
+    if (const char *e = getenv("DSA_SCORE_WAVES")) p.score_waves = atoi(e) == 8 ? 8 : 4;
     // DSA_SCORE_VALU=1: the decode scorer on v_dot2_f32_bf16 instead of MFMA
     // (k_score_valu; bf16 inputs), kept to measure the choice
     p.score_valu = 0;
