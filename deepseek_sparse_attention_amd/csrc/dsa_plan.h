@@ -143,9 +143,28 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     // step at C0, C4 and 2 x 128K, equal at 1 x 128K)
     const int64_t pair_target = n_q <= 2 ? 16 * (int64_t)n_q : 64;
     int64_t ns = p.attn_hs ? (pair_target + n_q - 1) / n_q : (n_q < 256 ? 256 / n_q : 1);
-    if (const char *e = getenv("DSA_ATTN_PAIRS")) ns = (atoi(e) + n_q - 1) / n_q;
+    const char *pairs_env = getenv("DSA_ATTN_PAIRS");
+    if (pairs_env) ns = (atoi(pairs_env) + n_q - 1) / n_q;
     int64_t sr = (p.sel_max + ns - 1) / ns;
     sr = (sr + 31) / 32 * 32;
+    if (p.attn_hs == 2 || p.attn_sel) {
+        // the wave-private kernels deal 16-row steps to their 4 waves in
+        // turn: splits of a multiple of 64 rows give every wave as many
+        // steps.  The kept rows (top_k) are split evenly, and an unpooled
+        // tail (up to kpool - 1 rows) goes to a split of its own (k-pool,
+        // 2,048 + 3 rows, one query: 17 splits of 128 rows, step 37.7 us,
+        // against 13 of 160, 38.3 us)
+        sr = (p.top_k + ns - 1) / ns;
+        sr = (sr + 63) / 64 * 64;
+        if (sr < 64) sr = 64;
+        // and at most 64 (query, split) pairs, so that the 4 head groups'
+        // work-groups (one per CU) run in one round of 256: with 3, 5 or 7
+        // queries the pairs had rounded up past 64, and a second round of
+        // work-groups doubled the attention (3 queries at 128K: attention
+        // with top-k 27.5 us with 22 splits of 96 rows, 16.6 with 16 of 128;
+        // 7 queries 33.1 vs 18.6 us)
+        while (!pairs_env && sr < kWvMaxRows && (int64_t)n_q * ((p.sel_max + sr - 1) / sr) > 64) sr += 64;
+    }
     if (sr < 64) sr = 64;
     if (sr > kMaxSplitRows) sr = kMaxSplitRows;
     if ((p.attn_hs == 2 || p.attn_sel) && sr > kWvMaxRows) sr = kWvMaxRows;
