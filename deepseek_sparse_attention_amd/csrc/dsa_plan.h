@@ -189,10 +189,15 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     while (tile > 256 && (int64_t)n_q * ((p.max_rows + tile - 1) / tile) < 128) tile >>= 1;
     // Between one and two work-groups per CU of 1,024-row tiles, some CUs
     // would take two and the rest one; 2,048-row tiles (with 8 waves, see
-    // below) give every busy CU one (3 queries at 128K: 42.8 vs 43.8 us)
+    // below) give every busy CU one (3 queries at 128K: 42.6 vs 43.7 us).
+    // Between two and four, the second round of work-groups would be partly
+    // empty; 4,096-row tiles with 8 waves run in one round (128K, us per
+    // step: 5 queries 55.8-56.0 vs 56.7, 6 queries 60.9 vs 61.3, 7 queries
+    // 67.0-67.2 vs 68.1-68.2; 8 queries, 1,024 tiles, gain nothing)
     {
         const int64_t n1024 = (int64_t)n_q * ((p.max_rows + 1023) / 1024);
         if (tile == 1024 && n1024 > 256 && n1024 < 512) tile = 2048;
+        if (tile == 1024 && n1024 > 512 && n1024 < 1024) tile = 4096;
     }
     if (const char *e = getenv("DSA_SCORE_TILE")) {   // tuning override: a power of two, 256 .. 8192
         const int t = atoi(e);
