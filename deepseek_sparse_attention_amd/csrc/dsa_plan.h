@@ -120,12 +120,14 @@ inline Plan make_plan(int32_t kpool, int32_t top_k, int32_t d_rope, int32_t n_q,
     // its top-k inside the wave-private attention, k_attend_sel: no
     // k_select launch and no selection round trip through memory.  Every
     // work-group repeats its query's selection, which beyond 8 queries
-    // costs more than the launch it saves (attention with top-k at 128K,
-    // us: 8 queries 24.0 fused vs 23.7 + a launch; 16: 36.3 vs 31.1; 64:
-    // 82.8 vs 71.7).  DSA_ATTN_SEL=0 keeps k_select + the attention kernel
-    // above instead.
+    // costs as much as the launch it saves or more (128K, us per step: 9,
+    // 12 and 16 queries the same either way, 87.7, 106 and 131; 64 queries,
+    // attention with top-k 82.8 vs 71.7 for k_select + k_attend_wv).
+    // DSA_ATTN_SEL=0 keeps k_select + the attention kernel above instead;
+    // DSA_ATTN_SEL=2 takes the fused kernel up to 64 queries.
     p.attn_sel = n_q <= 8 ? 1 : 0;
-    if (const char *e = getenv("DSA_ATTN_SEL")) p.attn_sel = p.attn_sel && atoi(e) != 0;
+    if (const char *e = getenv("DSA_ATTN_SEL"))
+        p.attn_sel = atoi(e) == 2 ? (n_q <= 64 ? 1 : 0) : p.attn_sel && atoi(e) != 0;
     // k_attend_sel takes the candidates of up to 64 chunks per query straight
     // into registers (16 chunks per wave): larger chunks when a query has more
     if (p.attn_sel) {
