@@ -50,3 +50,24 @@ def test_config_c3_full():
     for j in range(w.n_q):
         s = sel_g[j, :cnt_g[j]]
         assert cnt_g[j] == 2048 and np.all(np.diff(s) > 0) and s[-1] < w.q_nvis[j]
+
+
+@pytest.mark.parametrize("batch", [3, 5, 6])
+def test_decode_128k_batch_shapes(batch):
+    """Batches at 128K whose launch shapes differ from the 8-query point:
+    3 queries score 2,048-row tiles with 8-wave work-groups, 5 and 6
+    4,096-row tiles; their attention takes 16, 11 and 8 splits (at most 64
+    (query, split) pairs).  Every query against the oracle."""
+    t0 = time.time()
+    w = I.decode_128k(batch)
+    log(f"128K x {batch}: generated in {time.time() - t0:.1f}s")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, f"128K x {batch}")
+    check_attention(out_g, lse_g, out, lse, f"128K x {batch}")
