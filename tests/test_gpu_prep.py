@@ -154,6 +154,11 @@ F16_CASES = [
     ("tok_mixed", 2, 5003, [0, 1, 1, 0], [5003, 4097, 1500, 2049]),
     ("tok_prefill", 1, 4096, [0] * 24, list(range(4073, 4097))),
     ("tok_window", 2, 9000, [0, 0, 0, 1, 1, 1], [8998, 8999, 9000, 7000, 7001, 7002]),
+    # long contexts, whose decode scorer runs 8-wave work-groups: 1,024-row
+    # tiles for one query, 2,048 for three, 4,096 for five
+    ("tok_long1", 1, 131072, [0], [131072]),
+    ("tok_long3", 3, 131072, [0, 1, 2], [131072, 131000, 100003]),
+    ("tok_long5", 5, 131072, [0, 1, 2, 3, 4], [131072, 131071, 90000, 131072, 70001]),
 ]
 
 
