@@ -2568,10 +2568,11 @@ __global__ __launch_bounds__(256) void k_attend_sel(Args a) {
 }
 
 // Merge the splits of each (query, head): grid (64, n_q), 128 threads, each
-// thread four output columns.  Up to 16 splits are loaded in one round trip
-// and merged online (running max, rescaled sums).
+// thread four output columns.  Up to MB splits are loaded in one round trip
+// and merged online (running max, rescaled sums).  MB = 32 serves 17 to 32
+// splits (a k-pool query's 16 splits and its tail) in one round trip.
+template <int MB>
 __global__ __launch_bounds__(128) void k_reduce(Args a) {
-    constexpr int MB = 16;
     const int q = blockIdx.y, h = blockIdx.x, lane = lane_id();
     // the fused step's one-pass top-k read the query's first-digit histogram
     // from the scorer in the kernel before: work-group h clears bins
@@ -3014,7 +3015,10 @@ hipError_t launch_attend(const Args &a, hipStream_t st, const hipEvent_t *ev) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.n_split == 1) return e;
-    DSA_LAUNCH(ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, k_reduce, dim3(kHeads, a.n_q), dim3(128), st, a);
+    if (a.n_split > 16 && a.n_split <= 32)
+        DSA_LAUNCH(ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, k_reduce<32>, dim3(kHeads, a.n_q), dim3(128), st, a);
+    else
+        DSA_LAUNCH(ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, k_reduce<16>, dim3(kHeads, a.n_q), dim3(128), st, a);
     return hipGetLastError();
 }
 
