@@ -508,7 +508,8 @@ __global__ __launch_bounds__(256) void k_score_valu(Args a) {
 // of each tile, NB = max(1, P / 2) and s = w % (16 / P): every wave has work
 // however few queries the block holds, except half of them for a lone query.  Causality masks the scores and the histogram
 // per query (a query scores rows < rows(q)).  Per-query first-digit
-// histograms live in LDS as 16-bit counters, two to a word.
+// histograms live in LDS as 16-bit counters, two to a word (bins i and
+// i + 2048).
 constexpr int kPfTile = 128;     // key rows per LDS tile
 constexpr int kPfRange = 4096;   // key rows per work-group
 constexpr int kPfWaves = 16;     // waves per work-group (two per query of a full block)
@@ -611,8 +612,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_score_prefill(Args a) {
         if (row < my_rows) {
             srow[row] = score;
             if (hist) {
+                // word i holds bins i and i + 2048 (the order key's top bit:
+                // negative and positive scores), so that neighbouring bins,
+                // where a query's scores crowd, are different words and a
+                // wave's adds to them do not serialise on one address
                 const uint32_t bin = order_key(score) >> 20;
-                atomicAdd(&lh[slot][bin >> 1], 1u << (16 * (bin & 1)));
+                atomicAdd(&lh[slot][bin & (kHistBins / 2 - 1)], 1u << (16 * (bin / (kHistBins / 2))));
             }
         }
     };
@@ -670,10 +675,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_score_prefill(Args a) {
             const int qq = q0 + i / (kHistBins / 2);
             const uint32_t word = (&lh[0][0])[i];
             if (!word || qq >= q_end) continue;
-            const int bin = 2 * (i % (kHistBins / 2));
+            const int bin = i % (kHistBins / 2);
             uint32_t *gh = a.hist + (size_t)qq * kHistStride + bin;
             if (word & 0xFFFFu) atomicAdd(gh, word & 0xFFFFu);
-            if (word >> 16) atomicAdd(gh + 1, word >> 16);
+            if (word >> 16) atomicAdd(gh + kHistBins / 2, word >> 16);
         }
     }
 }
