@@ -71,3 +71,29 @@ def test_decode_128k_batch_shapes(batch):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(sel_g, cnt_g, sel, cnt, f"128K x {batch}")
     check_attention(out_g, lse_g, out, lse, f"128K x {batch}")
+
+
+@pytest.mark.parametrize("n_q", [9, 16, 64, 128])
+def test_decode_large_batches(n_q):
+    """Decode batches beyond the 8-query point, at 131,072 cached tokens:
+    the top-k leaves the attention kernel (k_select), the attention is
+    k_attend_wv with the splits widened to at most 64 (query, split) pairs
+    up to 64 queries and k_attend with 2 splits at 128.  Queries are dealt
+    over 8 sequences in turn (no two neighbours share one, so the batch is
+    a decode batch, not a prefill run) and each sees its own context
+    length.  Every query against the oracle."""
+    T = 131072
+    q_seq = np.arange(n_q) % 8
+    q_nvis = T - 97 * np.arange(n_q)
+    w = I.make_workload(f"large_{n_q}", 60 + n_q % 7, I.GEOM_TOKEN, 8, T, q_seq, q_nvis)
+    log(f"decode x {n_q}: workload ready")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, f"decode x {n_q}")
+    check_attention(out_g, lse_g, out, lse, f"decode x {n_q}")
