@@ -97,3 +97,24 @@ def test_decode_large_batches(n_q):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(sel_g, cnt_g, sel, cnt, f"decode x {n_q}")
     check_attention(out_g, lse_g, out, lse, f"decode x {n_q}")
+
+
+@pytest.mark.parametrize("window", [2, 5, 9])
+def test_verify_windows_full(window):
+    """Speculative verify windows at 131,072 cached tokens, 8 sequences of
+    `window` rows at their last positions (the prefill scorer with the
+    run-length hint, then the per-row chain): every row against the
+    oracle."""
+    w = I.decode_window(8, window)
+    log(f"verify windows 8 x {window} at 131072: workload ready")
+    dw = DeviceWorkload(w)
+    assert dw.batch.q_per_seq_hint == window
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, f"windows 8 x {window}")
+    check_attention(out_g, lse_g, out, lse, f"windows 8 x {window}")
