@@ -118,3 +118,24 @@ def test_verify_windows_full(window):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(sel_g, cnt_g, sel, cnt, f"windows 8 x {window}")
     check_attention(out_g, lse_g, out, lse, f"windows 8 x {window}")
+
+
+def test_kpool_batch_full():
+    """The k-pool variant (NoPE, pools of 4) for a batch: 4 sequences of
+    2^19 cached tokens whose queries see 2^19 - 1, 2^19 - 2, 2^19 - 3 and
+    2^19 - 4 tokens (pool tails of 3, 2, 1 and 0 tokens), so that the
+    attention splits and the tail split differ from the one-query C4 case.
+    Every query against the oracle."""
+    T = 1 << 19
+    w = I.make_workload("kpool_b4", 71, I.GEOM_KPOOL, 4, T, np.arange(4), [T - 1, T - 2, T - 3, T - 4])
+    log("k-pool x 4 at 2^19: workload ready")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, "k-pool x 4")
+    check_attention(out_g, lse_g, out, lse, "k-pool x 4")
