@@ -139,3 +139,26 @@ def test_kpool_batch_full():
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(sel_g, cnt_g, sel, cnt, "k-pool x 4")
     check_attention(out_g, lse_g, out, lse, "k-pool x 4")
+
+
+@pytest.mark.parametrize("top_k", [64, 4096])
+def test_decode_topk_widths_full(top_k):
+    """8 sequences of 131,072 tokens with the narrowest and widest top-k
+    the planner treats differently: 64 (one attention split, no merge) and
+    4,096 (the largest the library takes: twice the candidates in the
+    in-attention selection and 512-row splits).  Every query against the
+    oracle."""
+    T = 131072
+    g = dict(I.GEOM_TOKEN, top_k=top_k)
+    w = I.make_workload(f"k{top_k}_b8", 80 + top_k % 11, g, 8, T, np.arange(8), T - 1000 * np.arange(8))
+    log(f"top-k {top_k}, 8 x 131072: workload ready")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, f"top-k {top_k}")
+    check_attention(out_g, lse_g, out, lse, f"top-k {top_k}")
