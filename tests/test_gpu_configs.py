@@ -162,3 +162,23 @@ def test_decode_topk_widths_full(top_k):
     sel, cnt, out, lse = oracle_decode(w)
     check_selection(sel_g, cnt_g, sel, cnt, f"top-k {top_k}")
     check_attention(out_g, lse_g, out, lse, f"top-k {top_k}")
+
+
+def test_decode_longest_context():
+    """One query over 4,194,299 of 4,194,304 cached tokens (2^22 rows of
+    keys, 4.8 GB of latent cache): the top-k chunks grow to keep at most
+    1,024 per query, and row indices pass 2^21.  Selection bit-exact and
+    output within tolerance of the oracle."""
+    T = 1 << 22
+    w = I.make_workload("long4m", 90, I.GEOM_TOKEN, 1, T, [0], [T - 5])
+    log("one query at 2^22 tokens: workload ready")
+    dw = DeviceWorkload(w)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    sel_g, cnt_g = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+    out_g, lse_g = dw.out.cpu().numpy(), dw.lse.cpu().numpy()
+    del dw
+    torch.cuda.empty_cache()
+    sel, cnt, out, lse = oracle_decode(w)
+    check_selection(sel_g, cnt_g, sel, cnt, "2^22 tokens")
+    check_attention(out_g, lse_g, out, lse, "2^22 tokens")
